@@ -1,0 +1,533 @@
+/*
+ * fp4_oracle.c -- plain, slow CPU oracle for FP4 (E2M1) block-scaled
+ * quantisation and matrix multiply.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file; it shares no source, header, table or constant
+ * generator with the HIP path.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load it.
+ *
+ * Every number format below is written out from its definition, with scalar
+ * loops and, for the matrix product, FP64 accumulation.  Compile with
+ * -O2 -fno-fast-math -ffp-contract=off so that every FP32 operation written
+ * here rounds exactly once, as IEEE-754 binary32 round-to-nearest-even.
+ *
+ * Sources (the pages this oracle follows):
+ *   [P1] "Rubin架构FP4 GEMM深度解析" (yfxerp.com/news/178243):
+ *        §3.1 E2M1 with one mantissa bit, block scaling, E8M0 power-of-two
+ *        scales, GEMM result times the product of the two scales;
+ *        §4.2 epilogue C = (A_fp4 * B_fp4) * (scaleA * scaleB);
+ *        §5.2 two FP4 values per byte, order must be fixed explicitly.
+ *   [P2] NVFP4 video transcript (prism.simon-ai.net/article/7890):
+ *        MXFP4 = 32-value blocks with a power-of-two scale (a scale of 70
+ *        must become 64 or 128); NVFP4 = 16-value blocks, E4M3 block scale,
+ *        plus one FP32 tensor scale for the global range.
+ *   [P4] Ultralytics glossary "FP4" (ultralytics.com/ru/glossary/fp4),
+ *        "How FP4 works": the E2M1 value set {0, ±0.5, ±1, ±1.5, ±2, ±3,
+ *        ±4, ±6}; the block scale maps the block's largest magnitude to 6;
+ *        the worked example rounds |x|/scale to the nearest grid value and
+ *        dequantises as grid * sign * scale.
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes): round-to-nearest-even onto the grid; MXFP4 exponent = the
+ * smallest e with amax <= 6 * 2^e ("ceil"), with the OCP-style
+ * floor(log2 amax) - 2 rule as a second mode; E4M3 = bias 7, max 448, no
+ * infinities, rounding to nearest-even with saturation; NVFP4 tensor scale
+ * s_t = amax_t / (6 * 448); low nibble holds the even-K element.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <float.h>
+
+#define OR_FMT_MXFP4 0
+#define OR_FMT_NVFP4 1
+#define OR_FMT_MXFP4_OCP 2
+
+#define OR_DT_F32 0
+#define OR_DT_BF16 1
+
+/* ------------------------------------------------------------------ */
+/* E2M1 ([P4] "How FP4 works": the eight non-negative values; [P1] §3.1:
+ * 1 sign bit, 2 exponent bits, 1 mantissa bit, bias 1).               */
+/* ------------------------------------------------------------------ */
+
+/* Magnitude of each 3-bit code, written from the format: exponent field
+ * E = code>>1, mantissa bit M = code&1; E == 0 is subnormal (M * 0.5),
+ * otherwise (1 + M/2) * 2^(E-1). */
+double oracle_e2m1_value(int code)
+{
+    int mag = code & 7;
+    int E = mag >> 1, M = mag & 1;
+    double v = (E == 0) ? 0.5 * M : (1.0 + 0.5 * M) * ldexp(1.0, E - 1);
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest grid magnitude to y >= 0, ties to the even code (the grid's
+ * round-to-nearest-even); values beyond 6 land on 6 because 6 is then the
+ * nearest grid point.  Plain argmin over the eight candidates. */
+int oracle_e2m1_encode_mag(float y)
+{
+    if (y >= 6.0f)
+        return 7; /* at or past the top of the grid 6 is the nearest value */
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs((double)y - oracle_e2m1_value(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* The page's worked example ([P4]): nearest grid point by argmin, the
+ * first (lower) candidate winning a tie, as torch.argmin does. */
+static int e2m1_encode_mag_first(float y)
+{
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs((double)y - oracle_e2m1_value(c));
+        if (d < bestd) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* E8M0 ([P1] §3.1, §4.2: a pure power-of-two exponent byte).  Bias 127;
+ * byte 255 would be NaN and is never produced.                        */
+/* ------------------------------------------------------------------ */
+double oracle_e8m0_value(int byte) { return ldexp(1.0, byte - 127); }
+
+/* Default rule: the smallest e in [-127, 127] with amax <= 6 * 2^e, i.e.
+ * the power of two that maps the block maximum closest to 6 from below
+ * without clipping ([P4]: largest magnitude mapped to 6; [P2]: the scale
+ * must be a power of two).  Found by counting upward, exactly in FP64. */
+int oracle_mx_exponent(float amax)
+{
+    int e = -127;
+    while (e < 127 && (double)amax > 6.0 * ldexp(1.0, e))
+        ++e;
+    return e;
+}
+
+/* Second rule (the OCP MX choice the pages name in [P1] §3.1):
+ * e = floor(log2 amax) - 2, where 2 is E2M1's largest exponent, clamped to
+ * the E8M0 range; elements above 6 then saturate to 6. */
+int oracle_mx_exponent_ocp(float amax)
+{
+    if (amax == 0.0f)
+        return -127;
+    int ex;
+    (void)frexp((double)amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+    int e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* ------------------------------------------------------------------ */
+/* E4M3 ([P2]: NVFP4 block scale with 4 exponent and 3 mantissa bits).
+ * Reading: OCP FP8 E4M3 -- bias 7, subnormals, no infinity, only
+ * S.1111.111 is NaN, so the largest finite value is 448.             */
+/* ------------------------------------------------------------------ */
+double oracle_e4m3_value(int byte)
+{
+    int E = (byte >> 3) & 15, M = byte & 7;
+    double v = (E == 0) ? M * ldexp(1.0, -9) : (1.0 + M / 8.0) * ldexp(1.0, E - 7);
+    return (byte & 0x80) ? -v : v;
+}
+
+/* Nearest finite non-negative E4M3 value to r >= 0, ties to the even code;
+ * anything above 448 saturates to 448 (the nearest finite value). */
+int oracle_e4m3_encode(float r)
+{
+    if (r >= 448.0f)
+        return 0x7E; /* at or past the largest finite value, 448 is nearest */
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 127; ++c) { /* 0x7F is NaN */
+        double d = fabs((double)r - oracle_e4m3_value(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* BF16 <-> FP32: BF16 keeps the top 16 bits of an FP32; rounding to it is
+ * round-to-nearest-even on the dropped 16 bits (finite inputs).        */
+/* ------------------------------------------------------------------ */
+float oracle_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    /* Among the two BF16 neighbours (truncation and truncation + 1 ulp),
+     * take the nearer; on a tie take the one with an even last bit. */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lo = u & 0xFFFF0000u;
+    uint32_t hi = lo + 0x10000u;
+    float flo, fhi;
+    memcpy(&flo, &lo, 4);
+    memcpy(&fhi, &hi, 4);
+    /* Past the largest BF16 the upper neighbour is infinity, which rounding
+     * treats as the next power of two, 2^128. */
+    double vhi = isinf(fhi) ? copysign(ldexp(1.0, 128), fhi) : (double)fhi;
+    double dlo = fabs((double)f - (double)flo);
+    double dhi = fabs((double)f - vhi);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return ((lo >> 16) & 1) ? (uint16_t)(hi >> 16) : (uint16_t)(lo >> 16);
+}
+
+/* ------------------------------------------------------------------ */
+/* Scale-buffer layout (the library's documented byte order).  Scales
+ * live in tiles of 16 rows x 16 blocks = 256 bytes, tiles row-major over
+ * (row tile, block tile).  Inside a tile the byte of (row i, block q) is
+ * at 4*lane + byte with lane = 16*j + i, where j is the 32-element K
+ * chunk of a 128-element K step that holds the block:
+ *   MXFP4 (32-blocks): q = 4*s + j,           byte = s    (s = step 0..3)
+ *   NVFP4 (16-blocks): q = 8*h + 2*j + t,     byte = 2*h + t
+ * Padding rows and blocks hold 0.                                      */
+/* ------------------------------------------------------------------ */
+static int64_t block_size(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 32; }
+
+int64_t oracle_scale_bytes(int fmt, int64_t rows, int64_t K)
+{
+    int64_t KB = K / block_size(fmt);
+    return ((rows + 15) / 16) * ((KB + 15) / 16) * 256;
+}
+
+int64_t oracle_scale_offset(int fmt, int64_t rows, int64_t K, int64_t r, int64_t b)
+{
+    (void)rows;
+    int64_t KB = K / block_size(fmt);
+    int64_t KT = (KB + 15) / 16;
+    int64_t tile = (r / 16) * KT + b / 16;
+    int64_t i = r % 16, q = b % 16;
+    int64_t lane, byte;
+    if (fmt == OR_FMT_NVFP4) {
+        int64_t h = q / 8, j = (q / 2) % 4, t = q % 2;
+        lane = 16 * j + i;
+        byte = 2 * h + t;
+    } else {
+        int64_t s = q / 4, j = q % 4;
+        lane = 16 * j + i;
+        byte = s;
+    }
+    return tile * 256 + lane * 4 + byte;
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantisation.                                                        */
+/* ------------------------------------------------------------------ */
+static float load_elem(const void* x, int dt, int64_t idx)
+{
+    if (dt == OR_DT_BF16)
+        return oracle_bf16_to_f32(((const uint16_t*)x)[idx]);
+    return ((const float*)x)[idx];
+}
+
+/* NVFP4 tensor scale ([P2]: one FP32 scale for the global range).
+ * Reading: s_t = amax_t / (6 * 448) in FP32, so the block holding the
+ * tensor's largest magnitude gets the largest E4M3 scale; an all-zero
+ * tensor takes s_t = 1; s_t is kept at or above the smallest normal
+ * FP32 so the block-scale division stays finite. */
+float oracle_nvfp4_tensor_scale(float amax_t)
+{
+    if (amax_t == 0.0f)
+        return 1.0f;
+    float s = amax_t / 2688.0f;
+    if (s < FLT_MIN)
+        s = FLT_MIN;
+    return s;
+}
+
+float oracle_tensor_amax(const void* x, int dt, int64_t n)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(load_elem(x, dt, i));
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+/* Quantise one block of `bs` values.  Writes 4-bit codes (one per byte, in
+ * codes_out[0..bs)) and returns the scale byte.  `rule` is the format;
+ * s_t is the NVFP4 tensor scale (ignored for MXFP4). */
+static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* codes_out)
+{
+    float amax = 0.0f;
+    for (int k = 0; k < bs; ++k)
+        if (fabsf(v[k]) > amax) amax = fabsf(v[k]);
+
+    int sbyte;
+    if (rule == OR_FMT_NVFP4) {
+        /* r = (amax_b / 6) / s_t, two FP32 divisions; block scale = E4M3 of
+         * r; effective divisor d = E4M3(r) * s_t in FP32. */
+        float r = (amax / 6.0f) / s_t;
+        sbyte = oracle_e4m3_encode(r);
+        float d = (float)oracle_e4m3_value(sbyte) * s_t;
+        for (int k = 0; k < bs; ++k) {
+            int sign = signbit(v[k]) ? 8 : 0;
+            int mag = (sbyte == 0) ? 0 : oracle_e2m1_encode_mag(fabsf(v[k]) / d);
+            codes_out[k] = (uint8_t)(sign | mag);
+        }
+    } else {
+        int e = (rule == OR_FMT_MXFP4_OCP) ? oracle_mx_exponent_ocp(amax) : oracle_mx_exponent(amax);
+        sbyte = e + 127;
+        for (int k = 0; k < bs; ++k) {
+            int sign = signbit(v[k]) ? 8 : 0;
+            float y = ldexpf(fabsf(v[k]), -e);
+            codes_out[k] = (uint8_t)(sign | oracle_e2m1_encode_mag(y));
+        }
+    }
+    return sbyte;
+}
+
+/* Quantise a rows x K matrix (K contiguous).
+ *   codes:  rows x K/2 bytes, element 2i in bits 0-3 of byte i, 2i+1 in
+ *           bits 4-7 ([P1] §5.2 leaves the order open; this is the reading).
+ *   scales: the tiled layout above (oracle_scale_bytes bytes), or, when
+ *           scales_canon is non-NULL, additionally rows x K/bs canonical.
+ *   tensor_scale: NVFP4 only.  If ts_given, *tensor_scale is read;
+ *           otherwise it is computed from the whole operand and written.
+ * Returns 0, or -1 on a shape the formats do not define. */
+int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
+                    uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given)
+{
+    int bs = (int)block_size(fmt);
+    if (rows < 0 || K < 0 || K % bs != 0)
+        return -1;
+    float s_t = 1.0f;
+    if (fmt == OR_FMT_NVFP4) {
+        if (ts_given) {
+            s_t = *tensor_scale;
+        } else {
+            s_t = oracle_nvfp4_tensor_scale(oracle_tensor_amax(x, dt, rows * K));
+            *tensor_scale = s_t;
+        }
+    }
+    memset(scales, 0, (size_t)oracle_scale_bytes(fmt, rows, K));
+    int64_t KB = K / bs;
+    float v[32];
+    uint8_t c[32];
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            for (int k = 0; k < bs; ++k)
+                v[k] = load_elem(x, dt, r * K + b * bs + k);
+            int sb = quantize_block(v, bs, fmt, s_t, c);
+            scales[oracle_scale_offset(fmt, rows, K, r, b)] = (uint8_t)sb;
+            if (scales_canon)
+                scales_canon[r * KB + b] = (uint8_t)sb;
+            for (int k = 0; k < bs; k += 2)
+                codes[(r * K + b * bs + k) / 2] = (uint8_t)(c[k] | (c[k + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* Exact value of element (r, k) of a quantised matrix, without the tensor
+ * scale: E2M1(code) * block scale ([P4]: grid * sign * scale). */
+static double elem_value(const uint8_t* codes, const uint8_t* scales, int fmt, int64_t rows, int64_t K,
+                         int64_t r, int64_t k)
+{
+    int bs = (int)block_size(fmt);
+    uint8_t byte = codes[(r * K + k) / 2];
+    int code = (k & 1) ? (byte >> 4) : (byte & 15);
+    int sb = scales[oracle_scale_offset(fmt, rows, K, r, k / bs)];
+    double s = (fmt == OR_FMT_NVFP4) ? oracle_e4m3_value(sb) : oracle_e8m0_value(sb);
+    return oracle_e2m1_value(code) * s;
+}
+
+/* Dequantise to FP32 or BF16.  MXFP4: E2M1 * 2^(byte-127), exact.  NVFP4:
+ * (E2M1 * E4M3) * s_t -- the first product is exact, the second is one
+ * FP32 rounding.  BF16 output is the round-to-nearest-even of that FP32. */
+void oracle_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
+                       void* out, int out_dt, int64_t rows, int64_t K)
+{
+    double s_t = (fmt == OR_FMT_NVFP4) ? (double)*tensor_scale : 1.0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            /* p * s_t is exact in FP64 (<= 6 + 24 significant bits); the cast
+             * to float is then the single FP32 rounding. */
+            float f = (float)(elem_value(codes, scales, fmt, rows, K, r, k) * s_t);
+            if (out_dt == OR_DT_BF16)
+                ((uint16_t*)out)[r * K + k] = oracle_f32_to_bf16(f);
+            else
+                ((float*)out)[r * K + k] = f;
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* Matrix multiply ([P1] §1.1: FP4 inputs, FP32 accumulation; §3.1 and
+ * §4.2: result times the product of the scales).  The oracle is the exact
+ * definition evaluated in FP64:
+ *   C[m,n] = (sum_k A^[m,k] * B^[n,k]) * tsA * tsB
+ *   T[m,n] = (sum_k |A^[m,k] * B^[n,k]|) * |tsA * tsB|
+ * with A^, B^ the dequantised values without tensor scales.  A is M x K,
+ * B is N x K (one row per output column).  T bounds accumulation error:
+ * a result is accepted when |C - Cref| <= 1e-5 * T.                     */
+/* ------------------------------------------------------------------ */
+void oracle_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
+                 double tsB, int64_t M, int64_t N, int64_t K, int fmt, double* C, double* T)
+{
+    double ts = tsA * tsB;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = elem_value(A, sA, fmt, M, K, m, k) * elem_value(B, sB, fmt, N, K, n, k);
+                acc += p;
+                mag += fabs(p);
+            }
+            C[m * N + n] = acc * ts;
+            if (T) T[m * N + n] = mag * fabs(ts);
+        }
+}
+
+/* Only the listed output elements (rows[i], cols[i]); for sampled checks at
+ * sizes where the full product would take too long on the CPU. */
+void oracle_gemm_sampled(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
+                         double tsB, int64_t M, int64_t N, int64_t K, int fmt, const int64_t* rows,
+                         const int64_t* cols, int64_t count, double* C, double* T)
+{
+    double ts = tsA * tsB;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = elem_value(A, sA, fmt, M, K, rows[i], k) * elem_value(B, sB, fmt, N, K, cols[i], k);
+            acc += p;
+            mag += fabs(p);
+        }
+        C[i] = acc * ts;
+        if (T) T[i] = mag * fabs(ts);
+    }
+}
+
+/* Grouped product for mixture-of-experts layers ([P4], "Inference and
+ * training in FP4": MXFP4 expert weights).  Output row r belongs to the
+ * expert e with group_off[e] <= r < group_off[e+1]; it multiplies token
+ * row row_idx[r] of A (T_rows x K) by expert e's weights B_e (N x K,
+ * stored one expert after another, codes N*K/2 bytes and scales
+ * oracle_scale_bytes(fmt, N, K) bytes apart).  Only the listed
+ * (out_rows[i], cols[i]) are evaluated. */
+void oracle_gemm_grouped_sampled(const uint8_t* A, const uint8_t* sA, int64_t T_rows, const int32_t* row_idx,
+                                 const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
+                                 double tsA, double tsB, int64_t N, int64_t K, int fmt,
+                                 const int64_t* out_rows, const int64_t* cols, int64_t count, double* C,
+                                 double* T)
+{
+    double ts = tsA * tsB;
+    int64_t cb = N * K / 2, sbytes = oracle_scale_bytes(fmt, N, K);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t r = out_rows[i];
+        int32_t e = 0;
+        while (e < E && !(group_off[e] <= r && r < group_off[e + 1]))
+            ++e;
+        double acc = 0.0, mag = 0.0;
+        if (e < E) {
+            const uint8_t* Be = B + e * cb;
+            const uint8_t* sBe = sB + e * sbytes;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = elem_value(A, sA, fmt, T_rows, K, row_idx[r], k) *
+                           elem_value(Be, sBe, fmt, N, K, cols[i], k);
+                acc += p;
+                mag += fabs(p);
+            }
+        }
+        C[i] = acc * ts;
+        if (T) T[i] = mag * fabs(ts);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Mean absolute quantisation error of a vector at a given block size
+ * ([P4], worked example: whole tensor, then 32- and 16-value blocks).
+ *   mode 0 ("page"): scale = amax/6 in FP32, no scale encoding, nearest
+ *           grid point with the first candidate winning a tie,
+ *           dequantised = grid * sign * scale in FP32 -- the page's recipe.
+ *   mode 1: MXFP4 default exponent rule at this block size.
+ *   mode 2: MXFP4 OCP exponent rule at this block size.
+ *   mode 3: NVFP4 two-level scaling at this block size.
+ * The mean is taken in FP64.                                            */
+/* ------------------------------------------------------------------ */
+double oracle_block_mae(const float* x, int64_t n, int64_t bs, int mode)
+{
+    double sum = 0.0;
+    float s_t = 1.0f;
+    if (mode == 3)
+        s_t = oracle_nvfp4_tensor_scale(oracle_tensor_amax(x, OR_DT_F32, n));
+    for (int64_t b0 = 0; b0 < n; b0 += bs) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < bs; ++k)
+            if (fabsf(x[b0 + k]) > amax) amax = fabsf(x[b0 + k]);
+        for (int64_t k = 0; k < bs; ++k) {
+            float v = x[b0 + k];
+            float sign = (v > 0.0f) ? 1.0f : (v < 0.0f ? -1.0f : 0.0f);
+            float deq;
+            if (mode == 0) {
+                float scale = amax / 6.0f;
+                int c = e2m1_encode_mag_first(fabsf(v) / scale);
+                deq = (float)oracle_e2m1_value(c) * sign * scale;
+            } else if (mode == 3) {
+                float r = (amax / 6.0f) / s_t;
+                int sb = oracle_e4m3_encode(r);
+                float d = (float)oracle_e4m3_value(sb) * s_t;
+                int c = (sb == 0) ? 0 : oracle_e2m1_encode_mag(fabsf(v) / d);
+                deq = (float)((double)oracle_e2m1_value(c) * oracle_e4m3_value(sb) * (double)s_t) * sign;
+            } else {
+                int e = (mode == 2) ? oracle_mx_exponent_ocp(amax) : oracle_mx_exponent(amax);
+                int c = oracle_e2m1_encode_mag(ldexpf(fabsf(v), -e));
+                deq = (float)(oracle_e2m1_value(c) * ldexp(1.0, e)) * sign;
+            }
+            sum += fabs((double)deq - (double)v);
+        }
+    }
+    return sum / (double)n;
+}
+
+/* ------------------------------------------------------------------ */
+/* Batch helpers so the tests can sweep many inputs per call.          */
+/* ------------------------------------------------------------------ */
+void oracle_e2m1_encode_mag_batch(const float* y, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (uint8_t)oracle_e2m1_encode_mag(y[i]);
+}
+
+void oracle_e4m3_encode_batch(const float* r, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (uint8_t)oracle_e4m3_encode(r[i]);
+}
+
+void oracle_mx_exponent_batch(const float* amax, int64_t n, int ocp, int32_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ocp ? oracle_mx_exponent_ocp(amax[i]) : oracle_mx_exponent(amax[i]);
+}
+
+void oracle_f32_to_bf16_batch(const float* f, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(f[i]);
+}

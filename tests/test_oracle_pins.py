@@ -1,0 +1,335 @@
+"""The oracle's quantiser and matrix product pinned to what the pages fix:
+
+  * the glossary's worked example (Ultralytics "FP4", "How FP4 works"): its
+    printed mean absolute errors, reproduced from the same seed-0 vector;
+  * the error ordering whole-tensor > 32-block > 16-block in every mode;
+  * block max mapped to 6, power-of-two MXFP4 scales, NVFP4 two-level scales
+    (NVFP4 video transcript);
+  * the GEMM as FP32-accumulated product of scaled operands ("Rubin FP4 GEMM
+    deep dive", §3.1, §4.2): closed forms on hand-built operands and numpy's
+    matmul of dequantised operands on small shapes.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page_mae():
+    out = {}
+    with open(os.path.join(GOLDEN, "page_mae.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                b, v = line.split()
+                out[int(b)] = float(v)
+    return out
+
+
+def test_page_worked_example_reproduced(orc):
+    x = synth.page_vector()
+    assert x.size == 4096
+    for block, printed in _page_mae().items():
+        got = orc.block_mae(x, block, orc.MAE_PAGE)
+        assert round(got, 4) == printed, (block, got, printed)
+
+
+def test_nvfp4_whole_tensor_block_equals_page_recipe(orc):
+    # One block holding the whole tensor: its E4M3 scale is 448 and
+    # 448 * s_t = amax/6, so the two-level recipe collapses to the page's.
+    x = synth.page_vector()
+    assert round(orc.block_mae(x, 4096, orc.MAE_NVFP4), 4) == _page_mae()[4096]
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("which", ["page", "mxfp4_256"])
+def test_error_falls_as_blocks_shrink(orc, mode, which):
+    x = synth.page_vector() if which == "page" else synth.mxfp4_256_vector()
+    e = [orc.block_mae(x, b, mode) for b in (4096, 32, 16)]
+    assert e[0] > e[1] > e[2], e
+
+
+def _grid():
+    return np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _codes_unpacked(codes):
+    lo = codes & 15
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def _canon_from_tiled(orc, fmt, scales, rows, K):
+    KB = K // orc.block_size(fmt)
+    return np.array([[scales[orc.scale_offset(fmt, rows, K, r, b)] for b in range(KB)] for r in range(rows)],
+                    np.uint8)
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_mxfp4_scales_are_powers_of_two_and_max_maps_near_6(orc, fmt):
+    x = synth.gaussian(11, (64, 256), every=97)
+    codes, scales, canon, ts = orc.quantize(x, fmt)
+    assert ts == 1.0
+    np.testing.assert_array_equal(_canon_from_tiled(orc, fmt, scales, 64, 256), canon)
+    c = _codes_unpacked(codes).reshape(64, 8, 32)
+    blocks = x.reshape(64, 8, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = canon.astype(np.int64) - 127
+    # the decoded scale is a power of two and the block max lands on 4 or 6
+    ymax = amax / np.ldexp(1.0, e)
+    if fmt == 0:
+        assert np.all((ymax > 3.0) & (ymax <= 6.0))
+    else:
+        assert np.all((ymax >= 4.0) & (ymax < 8.0))
+    imax = np.abs(blocks).argmax(axis=2)
+    cmax = np.take_along_axis(c & 7, imax[..., None], axis=2)[..., 0]
+    # the block max rounds to 3, 4 or 6 (ceil rule, y in (3, 6]) or 4 or 6
+    # (floor rule, y in [4, 8) saturating at 6)
+    assert np.all(cmax >= (5 if fmt == 0 else 6))
+    # an amax of exactly 6*2^j gives scale 2^j and code 7
+    x2 = np.zeros((1, 32), np.float32)
+    x2[0, 5] = np.float32(6.0 * 2.0 ** -3)
+    x2[0, 7] = -0.1
+    codes2, _, canon2, _ = orc.quantize(x2, fmt)
+    assert canon2[0, 0] == 127 - 3
+    assert _codes_unpacked(codes2)[0, 5] == 7
+
+
+def test_nvfp4_block_max_gets_code_7(orc):
+    x = synth.row_scaled_gaussian(12, 64, 512)
+    codes, scales, canon, ts = orc.quantize(x, orc.FMT_NVFP4)
+    assert ts == np.float32(np.abs(x).max()) / np.float32(2688.0)
+    c = _codes_unpacked(codes).reshape(64, 32, 16)
+    blocks = np.abs(x.reshape(64, 32, 16))
+    imax = blocks.argmax(axis=2)
+    cmax = np.take_along_axis(c & 7, imax[..., None], axis=2)[..., 0]
+    normal = canon >= 8  # E4M3 exponent field > 0: relative error <= 2^-4
+    assert normal.sum() > 1000
+    assert np.all(cmax[normal] == 7)
+    # the block that holds the tensor max gets the largest finite E4M3 scale
+    r, k = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert canon[r, k // 16] == 0x7E
+
+
+def test_nvfp4_quantizer_steps_with_torch_e4m3(orc):
+    """Per block: r = (amax/6)/s_t in FP32, E4M3 by torch's cast, divisor
+    d = E4M3(r)*s_t in FP32, code = nearest grid point of |x|/d."""
+    import torch
+    x = synth.gaussian(13, (32, 128), std=0.3, every=41)
+    codes, scales, canon, ts = orc.quantize(x, orc.FMT_NVFP4)
+    f32 = np.float32
+    amax_t = np.abs(x).max()
+    assert ts == f32(amax_t) / f32(2688.0)
+    blocks = x.reshape(32, 8, 16)
+    amax = np.abs(blocks).max(axis=2).astype(f32)
+    r = (amax / f32(6.0)) / f32(ts)
+    sb = torch.from_numpy(r).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(canon, sb.view(torch.uint8).numpy())
+    d = sb.to(torch.float32).numpy() * f32(ts)
+    y = (np.abs(blocks) / d[..., None]).astype(f32)
+    dist = np.abs(y[..., None].astype(np.float64) - _grid())
+    srt = np.sort(dist, axis=-1)
+    tie = srt[..., 0] == srt[..., 1]
+    ref = np.argmin(dist, axis=-1)
+    got = (_codes_unpacked(codes).reshape(32, 8, 16) & 7)
+    assert not tie.any()
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantized_value_is_nearest_grid_point(orc, fmt):
+    x = synth.gaussian(14, (16, 512), every=33)
+    codes, scales, canon, ts = orc.quantize(x, fmt)
+    bs = orc.block_size(fmt)
+    deq = orc.dequantize(codes, scales, 1.0, fmt, 16, 512).astype(np.float64)
+    if fmt == 1:
+        s = np.array([[orc.e4m3_value(b) for b in row] for row in canon]) * ts
+    else:
+        s = np.ldexp(1.0, canon.astype(np.int64) - 127)
+    s = np.repeat(s, bs, axis=1)
+    grid = _grid()
+    # the chosen magnitude is at least as close to |x|/s as any grid point
+    y = np.abs(x.astype(np.float64)) / s
+    chosen = np.abs(deq) / (s / (ts if fmt == 1 else 1.0))
+    best = np.abs(y[..., None] - grid).min(axis=-1)
+    assert np.all(np.abs(chosen - y) <= best + 1e-12 * np.maximum(1, y))
+    # sign is the input's sign bit
+    signs = (_codes_unpacked(codes) >> 3).astype(bool)
+    np.testing.assert_array_equal(signs, np.signbit(x))
+
+
+def test_dequantize_is_grid_times_scale(orc):
+    x = synth.gaussian(15, (8, 64))
+    codes, scales, canon, _ = orc.quantize(x, orc.FMT_MXFP4)
+    c = _codes_unpacked(codes)
+    grid = _grid()
+    ref = np.where(c >= 8, -1.0, 1.0) * grid[c & 7] * np.repeat(np.ldexp(1.0, canon.astype(np.int64) - 127), 32,
+                                                                  axis=1)
+    np.testing.assert_array_equal(orc.dequantize(codes, scales, 1.0, 0, 8, 64), ref.astype(np.float32))
+    bf = orc.dequantize(codes, scales, 1.0, 0, 8, 64, out_bf16=True)
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(bf), ref.astype(np.float32))  # exact in BF16
+
+
+def test_nvfp4_dequantize_applies_tensor_scale_once(orc):
+    x = synth.gaussian(16, (4, 64), std=5.0)
+    codes, scales, canon, ts = orc.quantize(x, orc.FMT_NVFP4)
+    c = _codes_unpacked(codes)
+    v = np.where(c >= 8, -1.0, 1.0) * _grid()[c & 7] * np.repeat(
+        np.array([[orc.e4m3_value(b) for b in row] for row in canon]), 16, axis=1)
+    ref = (v.astype(np.float32) * np.float32(ts)).astype(np.float32)  # exact product, one FP32 rounding
+    np.testing.assert_array_equal(orc.dequantize(codes, scales, ts, 1, 4, 64), ref)
+
+
+def test_zero_and_negative_zero(orc):
+    x = np.zeros((2, 32), np.float32)
+    x[1, 3] = -0.0
+    for fmt in (0, 1, 2):
+        codes, scales, canon, ts = orc.quantize(x, fmt)
+        assert np.all(canon == 0)
+        c = _codes_unpacked(codes)
+        assert c[1, 3] == 8 and np.all(np.delete(c.reshape(-1), 32 + 3) == 0)
+        if fmt == 1:
+            assert ts == 1.0
+
+
+def test_bf16_input_is_its_fp32_value(orc):
+    x = synth.to_bf16_bits(synth.gaussian(17, (8, 128), every=50))
+    xf = synth.bf16_bits_to_f32(x)
+    for fmt in (0, 1):
+        a = orc.quantize(x, fmt)
+        b = orc.quantize(xf, fmt)
+        for u, v in zip(a[:3], b[:3]):
+            np.testing.assert_array_equal(u, v)
+        assert a[3] == b[3]
+
+
+# ---- matrix product ------------------------------------------------------
+def _pack(codes4):
+    codes4 = np.asarray(codes4, np.uint8)
+    return (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _scales_const(orc, fmt, rows, K, byte):
+    s = np.zeros(orc.scale_bytes(fmt, rows, K), np.uint8)
+    for r in range(rows):
+        for b in range(K // orc.block_size(fmt)):
+            s[orc.scale_offset(fmt, rows, K, r, b)] = byte
+    return s
+
+
+@pytest.mark.parametrize("fmt,unit", [(0, 127), (1, 0x38)])
+def test_gemm_closed_forms(orc, fmt, unit):
+    M, N, K = 3, 5, 256
+    # all elements 6 (code 7), unit scales: C = 36*K
+    A = _pack(np.full((M, K), 7))
+    B = _pack(np.full((N, K), 7))
+    sA = _scales_const(orc, fmt, M, K, unit)
+    sB = _scales_const(orc, fmt, N, K, unit)
+    C, T = orc.gemm(A, sA, B, sB, M, N, K, fmt)
+    np.testing.assert_array_equal(C, np.full((M, N), 36.0 * K))
+    np.testing.assert_array_equal(T, C)
+    # tensor scales multiply the result
+    C2, _ = orc.gemm(A, sA, B, sB, M, N, K, fmt, tsA=0.5, tsB=3.0)
+    np.testing.assert_array_equal(C2, 1.5 * C)
+    # alternating signs along K cancel exactly: +6 -6 +6 ...
+    alt = np.tile(np.array([7, 15], np.uint8), (N, K // 2))
+    C3, T3 = orc.gemm(A, sA, _pack(alt), sB, M, N, K, fmt)
+    np.testing.assert_array_equal(C3, 0.0)
+    np.testing.assert_array_equal(T3, 36.0 * K)
+    # one-hot: A[1, 70] = 1.5 (code 3), B[4, 70] = -4 (code 14), scales 2^3, 2^-2
+    a1 = np.zeros((M, K), np.uint8)
+    b1 = np.zeros((N, K), np.uint8)
+    a1[1, 70] = 3
+    b1[4, 70] = 14
+    if fmt == 0:
+        sA1 = _scales_const(orc, fmt, M, K, 127 + 3)
+        sB1 = _scales_const(orc, fmt, N, K, 127 - 2)
+        want = 1.5 * -4.0 * 2.0 ** 3 * 2.0 ** -2
+    else:
+        sA1 = _scales_const(orc, fmt, M, K, 0x50)   # 2^3
+        sB1 = _scales_const(orc, fmt, N, K, 0x2D)   # 1.625 * 2^-2
+        want = 1.5 * -4.0 * 8.0 * 1.625 * 0.25
+    C4, _ = orc.gemm(_pack(a1), sA1, _pack(b1), sB1, M, N, K, fmt)
+    ref = np.zeros((M, N))
+    ref[1, 4] = want
+    np.testing.assert_array_equal(C4, ref)
+
+
+def test_gemm_block_scale_doubling_adds_that_block(orc):
+    fmt, M, N, K = 0, 2, 3, 128
+    x = synth.gaussian(18, (M, K))
+    w = synth.gaussian(19, (N, K))
+    A, sA, cA, _ = orc.quantize(x, fmt)
+    B, sB, _, _ = orc.quantize(w, fmt)
+    C, _ = orc.gemm(A, sA, B, sB, M, N, K, fmt)
+    off = orc.scale_offset(fmt, M, K, 1, 2)  # row 1, block 2 (K 64..95)
+    sA2 = sA.copy()
+    sA2[off] += 1
+    C2, _ = orc.gemm(A, sA2, B, sB, M, N, K, fmt)
+    deqA = orc.dequantize(A, sA, 1.0, fmt, M, K).astype(np.float64)
+    deqB = orc.dequantize(B, sB, 1.0, fmt, N, K).astype(np.float64)
+    part = deqA[1, 64:96] @ deqB[:, 64:96].T
+    np.testing.assert_array_equal(C2[0], C[0])
+    np.testing.assert_allclose(C2[1] - C[1], part, rtol=0, atol=1e-12 * np.abs(part).max())
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 7, 64), (8, 3, 128), (16, 16, 256)])
+def test_gemm_equals_numpy_matmul_of_dequantised(orc, fmt, M, N, K):
+    x = synth.gaussian(20 + M, (M, K), every=13)
+    w = synth.gaussian(30 + N, (N, K), std=0.1)
+    A, sA, _, tA = orc.quantize(x, fmt)
+    B, sB, _, tB = orc.quantize(w, fmt)
+    C, T = orc.gemm(A, sA, B, sB, M, N, K, fmt, tsA=tA, tsB=tB)
+    dA = orc.dequantize(A, sA, 1.0, fmt, M, K).astype(np.float64)  # exact without tensor scale
+    dB = orc.dequantize(B, sB, 1.0, fmt, N, K).astype(np.float64)
+    ref = (dA @ dB.T) * tA * tB
+    np.testing.assert_allclose(C, ref, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(T, (np.abs(dA) @ np.abs(dB).T) * tA * tB, rtol=1e-12, atol=1e-300)
+    # sampled variant agrees element for element
+    rows = np.array([0, M - 1, M // 2])
+    cols = np.array([N - 1, 0, N // 2])
+    Cs, Ts = orc.gemm_sampled(A, sA, B, sB, M, N, K, fmt, rows, cols, tsA=tA, tsB=tB)
+    np.testing.assert_array_equal(Cs, C[rows, cols])
+    np.testing.assert_array_equal(Ts, T[rows, cols])
+
+
+def test_grouped_equals_per_expert_gemm(orc):
+    fmt, E, T_rows, N, K = 0, 4, 24, 16, 96
+    counts = np.array([5, 0, 17, 2])
+    row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=1)
+    x = synth.gaussian(40, (T_rows, K))
+    A, sA, _, _ = orc.quantize(x, fmt)
+    Bs, sBs = [], []
+    for e in range(E):
+        b, s, _, _ = orc.quantize(synth.gaussian(50 + e, (N, K), std=0.02), fmt)
+        Bs.append(b)
+        sBs.append(s)
+    B = np.concatenate([b.reshape(-1) for b in Bs])
+    sB = np.concatenate(sBs)
+    rows = np.repeat(np.arange(off[-1]), N)
+    cols = np.tile(np.arange(N), off[-1])
+    C, T = orc.gemm_grouped_sampled(A, sA, T_rows, row_idx, off, B, sB, N, K, fmt, rows, cols)
+    C = C.reshape(off[-1], N)
+    for e in range(E):
+        if counts[e] == 0:
+            continue
+        g = row_idx[off[e]:off[e + 1]]
+        Ag = orc.quantize(x[g], fmt)
+        Ce, _ = orc.gemm(Ag[0], Ag[1], Bs[e], sBs[e], len(g), N, K, fmt)
+        np.testing.assert_array_equal(C[off[e]:off[e + 1]], Ce)
+
+
+def test_tolerance_check_semantics(orc):
+    Cref = np.array([1.0, -2.0, 0.0, 100.0])
+    T = np.array([10.0, 10.0, 0.0, 1000.0])
+    ok = orc.gemm_within_tolerance(np.array([1.0 + 9e-5, -2.0 - 1.1e-4, 0.0, 100.0]), Cref, T)
+    np.testing.assert_array_equal(ok, [True, False, True, True])
+    bf = orc.f32_to_bf16_bits(np.array([1.0, -2.0, 0.0, 100.0], np.float32))
+    assert orc.gemm_within_tolerance(bf, Cref, T, out_bf16=True).all()
+    bad = orc.f32_to_bf16_bits(np.array([1.0078125, -2.0, 0.0, 100.0], np.float32))
+    np.testing.assert_array_equal(orc.gemm_within_tolerance(bad, Cref, T, out_bf16=True),
+                                  [False, True, True, True])
