@@ -1,0 +1,209 @@
+"""Python binding of libfp4 -- FP4 (E2M1) block-scaled quantisation and GEMM
+for AMD Instinct MI355X (gfx950).
+
+The C ABI (include/fp4.h) is exposed under the same names (``fp4_quantize``,
+``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_grouped``, ``fp4_scale_bytes``,
+``fp4_workspace_size``, ``fp4_status_string``), taking raw device pointers as
+integers.  The tensor helpers below only allocate outputs with torch and
+marshal ``data_ptr()`` / the current stream into those calls: every step of the
+computation runs in the HIP kernels of libfp4.so.  There is no fallback -- if
+the library is not built, or no GPU is present, the calls fail loudly.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp4.so")
+
+# enum fp4_fmt / fp4_dtype / fp4_op, flags
+MXFP4, NVFP4, MXFP4_OCP = 0, 1, 2
+F32, BF16 = 0, 1
+OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
+TS_GIVEN = 1
+
+FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_dequantize", "fp4_gemm",
+             "fp4_gemm_grouped", "fp4_status_string")
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, fp4_status_string(status), status))
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp4.so (built in-tree by block_scaled_fp4_03_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp4.so is not built (run python -m block_scaled_fp4_03_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        sig = {
+            "fp4_scale_bytes": (I64, [I32, I64, I64]),
+            "fp4_workspace_size": (SZ, [I32, I32, I64, I64, I64, I32]),
+            "fp4_quantize": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P, SZ, P]),
+            "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
+            "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
+            "fp4_gemm_grouped": (I32, [P, P, I64, P, P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
+            "fp4_status_string": (ctypes.c_char_p, [I32]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+# ---- raw C-ABI calls (integers for pointers) --------------------------------
+def fp4_status_string(status):
+    return lib().fp4_status_string(int(status)).decode()
+
+
+def fp4_scale_bytes(fmt, rows, K):
+    return lib().fp4_scale_bytes(fmt, rows, K)
+
+
+def fp4_workspace_size(op, fmt, M, N, K, E=0):
+    return lib().fp4_workspace_size(op, fmt, M, N, K, E)
+
+
+def fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace, workspace_bytes,
+                 stream):
+    return lib().fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
+                              workspace_bytes, stream)
+
+
+def fp4_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows, K, stream):
+    return lib().fp4_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows, K, stream)
+
+
+def fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, workspace_bytes, stream):
+    return lib().fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, workspace_bytes, stream)
+
+
+def fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, total_rows, N, K, fmt, out_dtype,
+                     workspace, workspace_bytes, stream):
+    return lib().fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, total_rows, N, K, fmt,
+                                  out_dtype, workspace, workspace_bytes, stream)
+
+
+# ---- torch helpers: allocation + pointer/stream marshalling only -------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise Fp4Error(rc, where)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def workspace(op, fmt, M, N, K, E=0, device="cuda"):
+    """A zero-filled workspace tensor of the size the operation needs (or None)."""
+    torch = _torch()
+    n = fp4_workspace_size(op, fmt, M, N, K, E)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+class Quantized:
+    """codes (rows x K/2 uint8), scales (tiled uint8), tensor_scale (1 float32 or None)."""
+
+    def __init__(self, codes, scales, tensor_scale, fmt, rows, K):
+        self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
+        self.fmt, self.rows, self.K = fmt, rows, K
+
+
+def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None):
+    """Quantise a 2-D float32/bfloat16 CUDA tensor along its last dimension.
+
+    NVFP4: pass `tensor_scale` (a 1-element float32 tensor) to use a given
+    scale; otherwise one is computed and returned in the result."""
+    torch = _torch()
+    rows, K = x.shape
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+        nbytes = fp4_scale_bytes(fmt, rows, K)
+        if nbytes < 0:
+            raise Fp4Error(int(nbytes), "fp4_scale_bytes")
+        scales = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ts = None
+        if fmt == NVFP4:
+            ts = tensor_scale if tensor_scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+        out = Quantized(codes, scales, ts, fmt, rows, K)
+    flags = TS_GIVEN if (fmt == NVFP4 and tensor_scale is not None) else 0
+    if fmt == NVFP4 and not flags and ws is None:
+        ws = workspace(OP_QUANTIZE, fmt, rows, 0, K, device=dev)
+    rc = fp4_quantize(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
+                      _dtype_code(x), flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "fp4_quantize")
+    return out
+
+
+def dequantize(q, out_dtype=None, stream=None):
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out = torch.empty((q.rows, q.K), dtype=out_dtype, device=q.codes.device)
+    rc = fp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.fmt, _ptr(out), _dtype_code(out),
+                        q.rows, q.K, _stream(stream))
+    _check(rc, "fp4_dequantize")
+    return out
+
+
+def gemm(a, b, out_dtype=None, out=None, ws=None, stream=None):
+    """C = A . B^T for quantised A (M x K) and B (N x K) of the same format."""
+    torch = _torch()
+    M, N, K = a.rows, b.rows, a.K
+    if b.K != K or a.fmt != b.fmt:
+        raise ValueError("operands disagree on K or format")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=a.codes.device)
+    if ws is None:
+        ws = workspace(OP_GEMM, a.fmt, M, N, K, device=a.codes.device)
+    rc = fp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(a.tensor_scale),
+                  _ptr(b.tensor_scale), _ptr(out), M, N, K, a.fmt, _dtype_code(out), _ptr(ws),
+                  0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "fp4_gemm")
+    return out
+
+
+def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_scale=None, out_dtype=None,
+                 out=None, ws=None, stream=None):
+    """Grouped (mixture-of-experts) GEMM; see fp4_gemm_grouped in include/fp4.h."""
+    torch = _torch()
+    E = group_off.numel() - 1
+    total = row_idx.numel()
+    if out is None:
+        out = torch.empty((total, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype,
+                          device=a.codes.device)
+    if ws is None:
+        ws = workspace(OP_GEMM_GROUPED, fmt, total, N, K, E, device=a.codes.device)
+    rc = fp4_gemm_grouped(_ptr(a.codes), _ptr(a.scales), a.rows, _ptr(row_idx), _ptr(group_off), E, _ptr(b_codes),
+                          _ptr(b_scales), _ptr(a.tensor_scale), _ptr(b_tensor_scale), _ptr(out), total, N, K, fmt,
+                          _dtype_code(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "fp4_gemm_grouped")
+    return out

@@ -1,0 +1,100 @@
+// fp4_device.h -- device-side number-format helpers shared by the libfp4
+// kernels (gfx950).  Internal header; not part of the C ABI.
+//
+// Formats (sources: Ultralytics glossary "FP4", "How FP4 works"; NVFP4 video
+// transcript, prism.simon-ai.net; "Rubin FP4 GEMM deep dive", yfxerp.com §3.1):
+//   E2M1: sign | 2-bit exponent (bias 1) | 1-bit mantissa, values 0..6.
+//   E8M0: power-of-two scale byte, 2^(byte - 127).
+//   E4M3: bias 7, 3-bit mantissa, subnormals, largest finite 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtMX = 0, kFmtNV = 1, kFmtMXOcp = 2;
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Magnitude code (0..7) of the E2M1 value nearest to y >= 0, ties to the even
+// code, saturating at 6: count the rounding boundaries y has passed.  A
+// boundary that is a tie is passed only when the code above it is even.
+__device__ __forceinline__ uint32_t e2m1_mag(float y) {
+  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) + (uint32_t)(y >= 1.75f) +
+         (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) + (uint32_t)(y > 5.0f);
+}
+
+// E8M0 byte of an MXFP4 block from its largest magnitude (finite, >= 0).
+// Default rule: the smallest e with amax <= 6 * 2^e.  With amax = m * 2^E,
+// m in [1, 2): e = E - 2 if m <= 1.5, else E - 1; zero and subnormal maxima
+// clamp to e = -127 (byte 0).  In FP32 bits: byte = max(0, exp_field - 2 +
+// (mantissa > 0x400000)).
+// OCP rule: e = floor(log2 amax) - 2, i.e. byte = max(0, exp_field - 2).
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  uint32_t u = f2u(amax);
+  int be = (int)(u >> 23);
+  int b = be - 2;
+  if (FMT == kFmtMX) b += ((u & 0x7FFFFFu) > 0x400000u) ? 1 : 0;
+  return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// E4M3 byte nearest to r >= 0 (ties to even), saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  if (!(r < 448.0f)) return 0x7Eu;                 // also catches +inf
+  if (r < 0.015625f) {                              // below 2^-6: step 2^-9
+    float m = __builtin_rintf(r * 512.0f);          // exact scaling, then RNE
+    return (uint32_t)m;                             // 8 -> 0x08 == 2^-6
+  }
+  uint32_t u = f2u(r);
+  uint32_t e = (u >> 23) - 127 + 7;                 // 1..15
+  uint32_t keep = (u >> 20) & 7u;
+  uint32_t rest = u & 0xFFFFFu;
+  uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+  uint32_t code = (e << 3) + keep + up;             // a carry bumps the exponent
+  return code;
+}
+
+// Value of a non-negative E4M3 byte (<= 0x7E) as FP32 (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;       // m * 2^-9
+  return u2f(((e + 120u) << 23) | (m << 20));       // (1 + m/8) * 2^(e-7)
+}
+
+// FP32 -> BF16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = f2u(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Byte offset of scale (row r, block b) in the tiled layout of a matrix with
+// KT = ceil(KB/16) block tiles per row tile.
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_offset(uint32_t r, uint32_t b, uint32_t KT) {
+  uint32_t tile = (r >> 4) * KT + (b >> 4);
+  uint32_t i = r & 15u, q = b & 15u;
+  uint32_t lane, byte;
+  if (FMT == kFmtNV) {
+    lane = 16u * ((q >> 1) & 3u) + i;
+    byte = 2u * (q >> 3) + (q & 1u);
+  } else {
+    lane = 16u * (q & 3u) + i;
+    byte = q >> 2;
+  }
+  return tile * 256u + lane * 4u + byte;
+}
+
+
+}  // namespace fp4

@@ -1,0 +1,37 @@
+// fp4_launch.h -- host-side launch entry points of the libfp4 kernels.
+// Internal header shared by the C-ABI layer (abi.cpp) and the kernel files.
+// Every function enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+// Quantisation (quantize.hip).
+hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* ws, float* tensor_scale,
+                              hipStream_t stream);
+hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
+                           const float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
+                             void* out, int out_dtype, int64_t rows, int64_t K, hipStream_t stream);
+
+// MXFP4 GEMM on the block-scaled FP4 matrix core (gemm_mx.hip).
+hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                          const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                          int out_dtype, hipStream_t stream);
+
+// NVFP4 GEMM / GEMV on the FP16 matrix core after exact decode (gemm_nv.hip).
+hipError_t launch_gemm_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                          const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                          int out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K);
+
+// Grouped MXFP4/NVFP4 GEMM (grouped.hip).
+hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
+                               const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
+                               const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N,
+                               int64_t K, int fmt, int out_dtype, void* workspace, hipStream_t stream);
+size_t gemm_grouped_workspace(int64_t total_rows, int64_t N, int64_t K, int32_t E);
+
+}  // namespace fp4

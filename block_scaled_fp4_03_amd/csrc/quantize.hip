@@ -1,0 +1,326 @@
+// quantize.hip -- FP32/BF16 -> MXFP4 / NVFP4 quantisers, tensor amax, and
+// dequantisation, for gfx950.
+//
+// Method (Ultralytics glossary "FP4", "How FP4 works"; NVFP4 video transcript,
+// prism.simon-ai.net): per block take the largest magnitude, choose the scale
+// that maps it to 6 (MXFP4: a power of two, E8M0; NVFP4: an E4M3 value under
+// one FP32 tensor scale), round each scaled element to the nearest E2M1 value
+// and pack two codes per byte ("Rubin FP4 GEMM deep dive", §5.2).
+//
+// Work mapping: one wavefront per (row, 512-element K slice).  Each lane owns 8
+// consecutive elements (32 B of FP32 or 16 B of BF16, one or two 16-byte
+// loads; a wavefront reads 2 KB / 1 KB contiguous), the block maximum is a
+// 4-lane (MXFP4) or 2-lane (NVFP4) butterfly, the lane writes its 4 code bytes
+// as one dword, and the scale bytes of the slice are gathered with cross-lane
+// shuffles into the dwords of the tiled layout, so every store is a dword.
+#include "fp4_device.h"
+#include "fp4_launch.h"
+
+#include <float.h>
+
+namespace fp4 {
+
+namespace {
+
+constexpr int kDtF32 = 0, kDtBF16 = 1;
+
+template <int DT>
+__device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
+  if (DT == kDtF32) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + idx);
+    const u32x4 a = __builtin_nontemporal_load(p);
+    const u32x4 b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = u2f(a[k]);
+      v[4 + k] = u2f(b[k]);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + idx);
+    const u32x4 a = __builtin_nontemporal_load(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = u2f(a[k] << 16);
+      v[2 * k + 1] = u2f(a[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Pack 8 already-scaled values into 8 E2M1 codes (element 2i in the low nibble
+// of byte i).  The gfx950 converter rounds x/1.0 to the nearest E2M1 value,
+// ties to even, saturating at +-6, and keeps the sign (so -0 and negative values
+// that round to zero give code 8).
+__device__ __forceinline__ uint32_t pack8(const float y[8]) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Tensor amax (NVFP4 tensor scale, NVFP4 video transcript: one FP32 scale for
+// the global range).  Grid-stride max, one atomicMax per workgroup on the
+// float's bit pattern (non-negative floats order like unsigned integers), and
+// the last workgroup to finish turns the maximum into s_t = amax / (6 * 448),
+// writes it, and clears the two workspace words for the next call.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, size_t n8,
+                                                          uint32_t* __restrict__ ws, float* __restrict__ ts) {
+  float m = 0.0f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    float v[8];
+    load8v<DT>(x, i * 8, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(&ws[0], f2u(m));
+    __threadfence();
+    uint32_t done = atomicAdd(&ws[1], 1u);
+    if (done == gridDim.x - 1) {
+      float amax = u2f(atomicOr(&ws[0], 0u));
+      float s = 1.0f;
+      if (amax > 0.0f) {
+        s = amax / 2688.0f;
+        if (s < FLT_MIN) s = FLT_MIN;
+      }
+      *ts = s;
+      ws[0] = 0u;
+      ws[1] = 0u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 quantiser.  Waves cover rows_pad = 16 * ceil(rows/16) rows so that the
+// padding rows of the scale tiles are written (as 0).
+// ---------------------------------------------------------------------------
+template <int FMT, int DT>
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales, uint32_t rows, uint32_t K,
+                                                          uint32_t KT, uint32_t total_waves) {
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t lane = threadIdx.x & 63u;
+  if (wave >= total_waves) return;
+  const uint32_t row = wave / KT, kt = wave % KT;
+  const uint32_t k0 = kt * 512u + lane * 8u;
+  const bool valid = row < rows && k0 < K;
+  float v[8];
+  if (valid) {
+    load8v<DT>(x, (size_t)row * K + k0, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  const uint32_t sbyte = mx_scale_byte<FMT>(am);  // 0 for padding (am == 0)
+  if (valid) {
+    // y = x * 2^-e with e = sbyte - 127: exact power of two, 2^(127 - e) is a
+    // normal float for every byte 0..253.
+    const float inv = u2f((254u - sbyte) << 23);
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = v[k] * inv;
+    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
+  }
+  // Scale dword for chunk j = lane (lanes 0..3): blocks q = j, 4+j, 8+j, 12+j of
+  // this slice, block q held by lane 4q.
+  const uint32_t j = lane & 3u;
+  const uint32_t b0 = __shfl(sbyte, 4 * j);
+  const uint32_t b1 = __shfl(sbyte, 4 * (4 + j));
+  const uint32_t b2 = __shfl(sbyte, 4 * (8 + j));
+  const uint32_t b3 = __shfl(sbyte, 4 * (12 + j));
+  if (lane < 4u) {
+    const uint32_t dw = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    const size_t off = ((size_t)(row >> 4) * KT + kt) * 256u + (16u * j + (row & 15u)) * 4u;
+    *reinterpret_cast<uint32_t*>(scales + off) = dw;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantiser.  One wave covers two 256-element scale tiles of one row
+// (lanes 0-31 the first, 32-63 the second).
+//   r = (amax_b / 6) / s_t; sb = E4M3(r); d = E4M3value(sb) * s_t;
+//   code = E2M1(x / d)   (x / inf = +-0 when sb == 0, so the block is all zero)
+// All divisions are IEEE FP32 round-to-nearest-even.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ tensor_scale, uint32_t rows,
+                                                          uint32_t K, uint32_t KT, uint32_t KT2,
+                                                          uint32_t total_waves) {
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t lane = threadIdx.x & 63u;
+  if (wave >= total_waves) return;
+  const uint32_t row = wave / KT2, kt2 = wave % KT2;
+  const uint32_t k0 = kt2 * 512u + lane * 8u;
+  const bool valid = row < rows && k0 < K;
+  const float s_t = *tensor_scale;
+  float v[8];
+  if (valid) {
+    load8v<DT>(x, (size_t)row * K + k0, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  const float r = (am / 6.0f) / s_t;
+  const uint32_t sb = e4m3_encode(r);
+  if (valid) {
+    const float d = (sb == 0u) ? __builtin_inff() : e4m3_value(sb) * s_t;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = v[k] / d;
+    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
+  }
+  // Tile t = lane / 32; dword for chunk j (lanes 32t + j, j < 4) holds blocks
+  // q = 2j, 2j+1, 8+2j, 9+2j of the tile; block q sits in lane 32t + 2q.
+  const uint32_t base = lane & 32u, j = lane & 3u;
+  const uint32_t c0 = __shfl(sb, base + 4 * j);
+  const uint32_t c1 = __shfl(sb, base + 4 * j + 2);
+  const uint32_t c2 = __shfl(sb, base + 16 + 4 * j);
+  const uint32_t c3 = __shfl(sb, base + 18 + 4 * j);
+  const uint32_t kt = 2u * kt2 + (lane >> 5);
+  if ((lane & 31u) < 4u && kt < KT) {
+    const uint32_t dw = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    const size_t off = ((size_t)(row >> 4) * KT + kt) * 256u + (16u * j + (row & 15u)) * 4u;
+    *reinterpret_cast<uint32_t*>(scales + off) = dw;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation: one lane per 8 elements.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float mag = (m < 2u) ? 0.5f * (float)m : u2f(((m >> 1) + 126u) << 23) * (1.0f + 0.5f * (float)(m & 1u));
+  return (c & 8u) ? -mag : mag;
+}
+
+template <int FMT, int OUT>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         const float* __restrict__ tensor_scale,
+                                                         void* __restrict__ out, uint32_t rows, uint32_t K,
+                                                         uint32_t KT) {
+  const size_t t = (size_t)blockIdx.x * 256u + threadIdx.x;
+  const uint32_t per_row = K / 8u;
+  if (t >= (size_t)rows * per_row) return;
+  const uint32_t row = (uint32_t)(t / per_row);
+  const uint32_t k0 = (uint32_t)(t % per_row) * 8u;
+  const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2);
+  const uint32_t bs = (FMT == kFmtNV) ? 16u : 32u;
+  const uint32_t sbyte = scales[scale_offset<FMT>(row, k0 / bs, KT)];
+  float o[8];
+  if (FMT == kFmtNV) {
+    const float s = e4m3_value(sbyte);
+    const float st = *tensor_scale;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = (e2m1_value(cw >> (4 * k)) * s) * st;
+  } else {
+    const int e = (int)sbyte - 127;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = __builtin_ldexpf(e2m1_value(cw >> (4 * k)), e);
+  }
+  const size_t idx = (size_t)row * K + k0;
+  if (OUT == kDtF32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + idx);
+    p[0] = float4{o[0], o[1], o[2], o[3]};
+    p[1] = float4{o[4], o[5], o[6], o[7]};
+  } else {
+    uint4 w;
+    w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    w.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+    w.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* ws, float* tensor_scale,
+                              hipStream_t stream) {
+  const size_t n8 = (size_t)n / 8;
+  size_t blocks = (n8 + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  if (in_dtype == kDtF32)
+    tensor_amax_kernel<kDtF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
+  else
+    tensor_amax_kernel<kDtBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
+                           const float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const uint32_t rows_pad = (r + 15u) / 16u * 16u;
+  if (fmt == kFmtNV) {
+    const uint32_t KT = (k / 16u + 15u) / 16u, KT2 = (KT + 1u) / 2u;
+    const uint32_t waves = rows_pad * KT2;
+    const dim3 grid((waves + 3u) / 4u);
+    if (in_dtype == kDtF32)
+      quantize_nv_kernel<kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                 waves);
+    else
+      quantize_nv_kernel<kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                  waves);
+  } else {
+    const uint32_t KT = (k / 32u + 15u) / 16u;
+    const uint32_t waves = rows_pad * KT;
+    const dim3 grid((waves + 3u) / 4u);
+    if (fmt == kFmtMX) {
+      if (in_dtype == kDtF32)
+        quantize_mx_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+      else
+        quantize_mx_kernel<kFmtMX, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+    } else {
+      if (in_dtype == kDtF32)
+        quantize_mx_kernel<kFmtMXOcp, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+      else
+        quantize_mx_kernel<kFmtMXOcp, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
+                             void* out, int out_dtype, int64_t rows, int64_t K, hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const size_t threads = (size_t)r * (k / 8u);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (fmt == kFmtNV) {
+    const uint32_t KT = (k / 16u + 15u) / 16u;
+    if (out_dtype == kDtF32)
+      dequantize_kernel<kFmtNV, kDtF32><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
+    else
+      dequantize_kernel<kFmtNV, kDtBF16><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
+  } else {
+    const uint32_t KT = (k / 32u + 15u) / 16u;
+    if (out_dtype == kDtF32)
+      dequantize_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
+    else
+      dequantize_kernel<kFmtMX, kDtBF16><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4

@@ -1,0 +1,171 @@
+/*
+ * fp4.h -- C ABI of libfp4: FP4 (E2M1) block-scaled quantisation and matrix
+ * multiply on AMD Instinct MI355X (gfx950).
+ *
+ * The operation, as the sources state it:
+ *   - E2M1 elements {0, ±0.5, ±1, ±1.5, ±2, ±3, ±4, ±6}, one scale per block
+ *     chosen so the block's largest magnitude maps to 6 (Ultralytics glossary
+ *     "FP4", "How FP4 works");
+ *   - MXFP4: 32-value blocks, power-of-two E8M0 scale; NVFP4: 16-value blocks,
+ *     E4M3 scale plus one FP32 per-tensor scale (NVFP4 video transcript,
+ *     prism.simon-ai.net; glossary "How FP4 works");
+ *   - the GEMM accumulates in FP32 and multiplies by the product of the scales,
+ *     C = (A_fp4 * B_fp4) * (scaleA * scaleB) ("Rubin FP4 GEMM deep dive",
+ *     yfxerp.com, §1.1, §3.1, §4.2);
+ *   - two FP4 values per byte with an explicitly fixed order, scales stored in
+ *     the order the kernel tiles read them (same page, §4.2, §5.2).
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent) unless
+ *     stated otherwise; `stream` is a hipStream_t passed as void* (NULL = the
+ *     null stream).  Every call is asynchronous on `stream`: it enqueues work
+ *     and returns; nothing is copied to or from the host, no call synchronises.
+ *   - The caller owns and allocates every buffer, workspace included.  The
+ *     library never allocates or frees memory and keeps no global mutable state.
+ *   - Argument errors return a negative fp4_status before any HIP call is made,
+ *     so they are reported synchronously and leave the stream untouched.  A
+ *     failed kernel launch returns FP4_ERR_HIP.  Faults inside a kernel surface
+ *     at the caller's next synchronisation.
+ *   - Matrices are row-major.  A quantised matrix of `rows` x `K` values is
+ *       codes:  rows * K/2 bytes; element k of a row is in byte k/2, bits 0-3
+ *               for even k and bits 4-7 for odd k; a code is sign<<3 | magnitude
+ *               with magnitude 0..7 -> 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ *       scales: fp4_scale_bytes(fmt, rows, K) bytes in the tiled layout below;
+ *       tensor scale (NVFP4 only): one FP32 in device memory.
+ *   - Element value: MXFP4  E2M1(code) * 2^(scale_byte - 127);
+ *                    NVFP4  E2M1(code) * E4M3(scale_byte) * tensor_scale.
+ *
+ * Tiled scale layout (identical for A and B operands; both are "rows x K").
+ *   A row has KB = K / bs blocks (bs = 32 for MXFP4, 16 for NVFP4).  Scales are
+ *   grouped in tiles of 16 rows x 16 blocks, 256 bytes each, stored row-tile
+ *   major: tile (rt, kt) starts at byte 256 * (rt * ceil(KB/16) + kt).  Inside
+ *   a tile, view the 256 bytes as 64 dwords ("lanes"); the block of row
+ *   16*rt + i that covers 32-value chunk j (j = 0..3) of a 128-value K step
+ *   sits in lane 16*j + i, and the byte within the lane is:
+ *     MXFP4: the K step s = 0..3 within the tile   (block q = 4*s + j)
+ *     NVFP4: 2*h + t, h = K step 0..1 within the tile, t = first or second
+ *            16-block of the 32-value chunk          (block q = 8*h + 2*j + t)
+ *   so one dword load per lane yields the scales one wavefront needs for four
+ *   (MXFP4) or two (NVFP4) K steps of a 16-row matrix-core operand.  Bytes of
+ *   rows >= `rows` or blocks >= KB are padding; the quantiser writes them as 0.
+ */
+#ifndef FP4_H_
+#define FP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block format. */
+enum fp4_fmt {
+    FP4_MXFP4 = 0,     /* 32-blocks, E8M0; exponent = smallest e with amax <= 6*2^e */
+    FP4_NVFP4 = 1,     /* 16-blocks, E4M3 (bias 7, max 448) + FP32 tensor scale      */
+    FP4_MXFP4_OCP = 2  /* 32-blocks, E8M0; exponent = floor(log2 amax) - 2, saturate */
+};
+
+/* Element type of unquantised inputs and of outputs. */
+enum fp4_dtype { FP4_F32 = 0, FP4_BF16 = 1 };
+
+/* Operation selector for fp4_workspace_size. */
+enum fp4_op { FP4_OP_QUANTIZE = 0, FP4_OP_GEMM = 1, FP4_OP_GEMM_GROUPED = 2 };
+
+/* Flags for fp4_quantize. */
+#define FP4_TS_GIVEN 1u /* NVFP4: read the tensor scale from *tensor_scale instead of computing it */
+
+enum fp4_status {
+    FP4_OK = 0,
+    FP4_ERR_NULL = -1,      /* a required pointer is NULL                          */
+    FP4_ERR_SHAPE = -2,     /* negative size, K not a multiple of the block, ...   */
+    FP4_ERR_ALIGN = -3,     /* a pointer is not aligned as documented              */
+    FP4_ERR_FMT = -4,       /* unknown fmt, or fmt not supported by this operation */
+    FP4_ERR_DTYPE = -5,     /* unknown dtype                                       */
+    FP4_ERR_WORKSPACE = -6, /* workspace missing or smaller than required          */
+    FP4_ERR_HIP = -7,       /* a HIP launch failed                                 */
+    FP4_ERR_FLAGS = -8      /* unknown flag bits                                   */
+};
+
+/* Size in bytes of the tiled scale buffer of a rows x K matrix, or a negative
+ * fp4_status for an invalid fmt or shape.  Host-only, no HIP call. */
+int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
+
+/* Workspace bytes an operation needs (0 if none).  For FP4_OP_QUANTIZE, M is
+ * the row count; for FP4_OP_GEMM_GROUPED, E is the expert count and M the total
+ * routed rows.  A workspace must be zero-filled once before its first use; every
+ * call leaves it zero-filled again when its work on the stream completes.
+ * Calls that share one workspace must be ordered (same stream, or events).
+ * Host-only. */
+size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E);
+
+/* Quantise a rows x K matrix x (K contiguous) of `in_dtype` (FP32 or BF16).
+ *   Per block: MXFP4 picks an E8M0 exponent from the block's largest magnitude;
+ *   NVFP4 takes r = (amax_block / 6) / tensor_scale, rounds it to E4M3 (nearest
+ *   even, saturating at 448), and divides by d = E4M3(r) * tensor_scale (FP32).
+ *   Each element is then rounded to the nearest E2M1 value, ties to even,
+ *   saturating at 6; the sign bit is copied (-0 gives code 8).
+ *   NVFP4 tensor scale: unless flags has FP4_TS_GIVEN, computed over the whole
+ *   matrix as s_t = amax / 2688 (6 * 448), s_t = 1 for an all-zero matrix and
+ *   s_t >= FLT_MIN, and written to *tensor_scale.  With FP4_TS_GIVEN the caller's
+ *   value is used (it must be a positive, finite, normal FP32).
+ *   (Sources: glossary "How FP4 works"; NVFP4 video transcript.)
+ * Requirements: K % bs == 0; x 16-byte aligned and K*elem_size % 16 == 0;
+ *   codes 16-byte aligned with K % 32 == 0 (so rows are whole 16-byte units);
+ *   block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
+ *   is ignored for MXFP4.  NVFP4 without FP4_TS_GIVEN needs a workspace of
+ *   fp4_workspace_size(FP4_OP_QUANTIZE, ...) bytes; otherwise workspace may be NULL.
+ * rows == 0 or K == 0 is a no-op. */
+int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                 int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Dequantise codes + scales (+ NVFP4 tensor scale) to a rows x K matrix of
+ * `out_dtype`.  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,
+ * times tensor_scale with one FP32 rounding; BF16 output is the round-to-
+ * nearest-even of that FP32 value.  Same alignment rules as fp4_quantize. */
+int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt,
+                   void* out, int out_dtype, int64_t rows, int64_t K, void* stream);
+
+/* C[M x N] = (sum_k A[m,k] * B[n,k]) * tsA * tsB, accumulated in FP32.
+ *   A: M x K quantised (codes + scales), B: N x K quantised (each row of B is one
+ *   output column, i.e. B is the weight matrix stored K-contiguous).
+ *   tsA, tsB: device FP32 tensor scales; required for NVFP4, optional (NULL = 1)
+ *   for MXFP4.  C: M x N row-major, FP32 or BF16 (round to nearest even).
+ *   MXFP4 runs on the gfx950 block-scaled FP4 matrix core with the E8M0 scales
+ *   applied inside the instruction; NVFP4 decodes E2M1 * E4M3 exactly to FP16
+ *   and runs the FP16 matrix core, with the tensor scales in the epilogue.
+ * Requirements: K % 32 == 0 (both formats); codes 16-byte aligned; scales
+ *   4-byte aligned; C aligned to its element size.  M, N >= 0 arbitrary.
+ *   workspace: fp4_workspace_size(FP4_OP_GEMM, ...) bytes (may be 0 -> NULL ok).
+ * M == 0 or N == 0 is a no-op; K == 0 writes zeros. */
+int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* tsA,
+             const float* tsB, void* C, int64_t M, int64_t N, int64_t K, int fmt, int out_dtype,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped GEMM for mixture-of-experts layers (glossary "Inference and training
+ * in FP4": MXFP4 expert weights).
+ *   A: A_rows x K quantised token rows.  row_idx[total_rows] (device int32):
+ *   output row r reads token row row_idx[r] of A.  group_off[E+1] (device int32,
+ *   non-decreasing, group_off[0] = 0, group_off[E] = total_rows): rows
+ *   group_off[e] .. group_off[e+1]-1 belong to expert e.  B: E expert matrices,
+ *   each N x K quantised, codes N*K/2 bytes apart and scales
+ *   fp4_scale_bytes(fmt, N, K) bytes apart.  C: total_rows x N, row r =
+ *   (A[row_idx[r]] . B_e^T) * tsA * tsB for its expert e.
+ *   Group sizes stay on the device; the kernel builds its own tile list.
+ *   Every row_idx entry must lie in [0, A_rows).
+ * Requirements as fp4_gemm; workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
+ *   fmt, total_rows, N, K, E) bytes. */
+int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
+                     const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
+                     const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N, int64_t K,
+                     int fmt, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* fp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H_ */

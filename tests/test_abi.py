@@ -1,0 +1,140 @@
+"""The C ABI library loads, exports every entry point include/fp4.h declares,
+and rejects bad arguments synchronously, before any HIP call (so these run
+without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_03_amd as fp4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "fp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(fp4_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fp4.LIB_PATH):
+        import block_scaled_fp4_03_amd.build as b
+        b.build()
+    return fp4.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert set(names) == set(fp4.FUNCTIONS), names
+    for n in names:
+        assert hasattr(L, n), n
+        assert isinstance(getattr(L, n), ctypes._CFuncPtr)
+
+
+def test_status_strings(L):
+    for s in range(0, -9, -1):
+        assert fp4.fp4_status_string(s).startswith("FP4_")
+    assert "unknown" in fp4.fp4_status_string(5)
+
+
+def test_scale_bytes(L):
+    assert fp4.fp4_scale_bytes(fp4.MXFP4, 256, 256) == 16 * 1 * 256
+    assert fp4.fp4_scale_bytes(fp4.NVFP4, 8192, 8192) == 512 * 32 * 256
+    assert fp4.fp4_scale_bytes(fp4.MXFP4, 5760, 2880) == 360 * 6 * 256
+    assert fp4.fp4_scale_bytes(fp4.MXFP4, 17, 96) == 2 * 1 * 256
+    assert fp4.fp4_scale_bytes(fp4.MXFP4, 4, 48) == -2  # K % 32
+    assert fp4.fp4_scale_bytes(fp4.NVFP4, 4, 48) == 256
+    assert fp4.fp4_scale_bytes(7, 4, 64) == -4
+    assert fp4.fp4_scale_bytes(fp4.MXFP4, -1, 64) == -2
+
+
+def test_scale_bytes_agrees_with_oracle(L, orc):
+    for fmt in (0, 1, 2):
+        for rows, K in [(1, 32), (16, 512), (33, 2880), (100, 4096)]:
+            assert fp4.fp4_scale_bytes(fmt, rows, K) == orc.scale_bytes(fmt, rows, K)
+
+
+def test_workspace_sizes(L):
+    assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.MXFP4, 10, 0, 64) == 0
+    assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.NVFP4, 10, 0, 64) == 8
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.MXFP4, 8192, 8192, 8192) == 0
+
+
+FAKE = 0x100000  # 16-byte-aligned fake device address: never dereferenced on the error paths
+ODD = FAKE + 2
+
+
+def test_quantize_argument_errors(L):
+    q = fp4.fp4_quantize
+    # fmt, dtype, flags
+    assert q(FAKE, 9, FAKE, FAKE, FAKE, 4, 64, 0, 0, None, 0, None) == -4
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, 4, 64, 3, 0, None, 0, None) == -5
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, 4, 64, 0, 4, None, 0, None) == -8
+    # shapes
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, -1, 64, 0, 0, None, 0, None) == -2
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, 4, 48, 0, 0, None, 0, None) == -2   # MXFP4 needs K % 32
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 40, 0, 0, None, 0, None) == -2   # NVFP4 needs K % 16
+    # empty is a no-op even with NULL pointers
+    assert q(None, 0, None, None, None, 0, 64, 0, 0, None, 0, None) == 0
+    assert q(None, 1, None, None, None, 5, 0, 0, 0, None, 0, None) == 0
+    # NULLs
+    assert q(None, 0, FAKE, FAKE, None, 4, 64, 0, 0, None, 0, None) == -1
+    assert q(FAKE, 1, FAKE, FAKE, None, 4, 64, 0, 0, FAKE, 8, None) == -1   # NVFP4 needs tensor_scale
+    # alignment
+    assert q(ODD, 0, FAKE, FAKE, None, 4, 64, 0, 0, None, 0, None) == -3
+    assert q(FAKE, 0, ODD, FAKE, None, 4, 64, 0, 0, None, 0, None) == -3
+    # NVFP4 computing its tensor scale needs the workspace
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 0, None, 0, None) == -6
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 0, FAKE, 4, None) == -6
+
+
+def test_dequantize_argument_errors(L):
+    d = fp4.fp4_dequantize
+    assert d(FAKE, FAKE, None, 5, FAKE, 0, 4, 64, None) == -4
+    assert d(FAKE, FAKE, None, 0, FAKE, 2, 4, 64, None) == -5
+    assert d(FAKE, FAKE, None, 0, FAKE, 0, 4, 50, None) == -2
+    assert d(FAKE, FAKE, None, 1, FAKE, 0, 4, 64, None) == -1
+    assert d(None, None, None, 0, None, 0, 0, 64, None) == 0
+    assert d(FAKE, FAKE, None, 0, ODD, 0, 4, 64, None) == -3
+
+
+def test_gemm_argument_errors(L):
+    g = fp4.fp4_gemm
+    args = dict(A=FAKE, sA=FAKE, B=FAKE, sB=FAKE, tsA=None, tsB=None, C=FAKE, M=4, N=4, K=64, fmt=0, out=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return g(a["A"], a["sA"], a["B"], a["sB"], a["tsA"], a["tsB"], a["C"], a["M"], a["N"], a["K"], a["fmt"],
+                 a["out"], None, 0, None)
+
+    assert call(fmt=4) == -4
+    assert call(out=7) == -5
+    assert call(K=48) == -2            # K % 32 for the GEMM
+    assert call(M=-1) == -2
+    assert call(M=0, C=None) == 0      # empty output: no-op
+    assert call(C=None) == -1
+    assert call(A=None) == -1
+    assert call(fmt=1) == -1           # NVFP4 needs both tensor scales
+    assert call(A=ODD) == -3
+    assert call(C=FAKE + 1, out=1) == -3
+
+
+def test_grouped_argument_errors(L):
+    g = fp4.fp4_gemm_grouped
+
+    def call(**kw):
+        a = dict(A=FAKE, sA=FAKE, A_rows=8, row_idx=FAKE, off=FAKE, E=2, B=FAKE, sB=FAKE, tsA=None, tsB=None, C=FAKE,
+                 total=8, N=16, K=64, fmt=0, out=1)
+        a.update(kw)
+        return g(a["A"], a["sA"], a["A_rows"], a["row_idx"], a["off"], a["E"], a["B"], a["sB"], a["tsA"], a["tsB"],
+                 a["C"], a["total"], a["N"], a["K"], a["fmt"], a["out"], None, 0, None)
+
+    assert call(fmt=3) == -4
+    assert call(K=40) == -2
+    assert call(E=-1) == -2
+    assert call(total=0) == 0
+    assert call(row_idx=None) == -1
+    assert call(off=FAKE + 2) == -3

@@ -1,0 +1,159 @@
+"""GPU GEMM parity against the oracle's FP64 product of the oracle-quantised
+operands: every output element within 1e-5 * sum|a*b| (FP32 outputs) or inside
+the BF16-rounded acceptance interval (BF16 outputs); closed forms bit-exact."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import assert_gemm_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_both(orc, x, fmt):
+    """Quantise on the GPU and in the oracle; the bits must agree."""
+    import block_scaled_fp4_03_amd as fp4
+    q = fp4.quantize(to_dev(x), fmt)
+    ref = orc.quantize(x, fmt)
+    np.testing.assert_array_equal(to_host(q.codes), ref[0])
+    np.testing.assert_array_equal(to_host(q.scales), ref[1])
+    return q, ref
+
+
+def _gemm_case(orc, fmt, M, N, K, bf16_out, seed, a_std=1.0, b_std=1.0):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    a = synth.gaussian(seed, (M, K), std=a_std, every=512 if M * K >= 512 else None)
+    b = synth.gaussian(seed + 1, (N, K), std=b_std, bernoulli=0.002)
+    say("gemm fmt=%d M=%d N=%d K=%d bf16=%s" % (fmt, M, N, K, bf16_out))
+    qa, ra = _quant_both(orc, a, fmt)
+    qb, rb = _quant_both(orc, b, fmt)
+    C = fp4.gemm(qa, qb, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, fmt, tsA=ra[3], tsB=rb[3])
+    assert_gemm_close(orc, to_host(C), Cref, T, bf16_out, "fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+
+
+MX_SHAPES = [(256, 256, 256), (1, 1, 32), (17, 33, 96), (300, 260, 544), (512, 512, 1024), (257, 513, 2880),
+             (64, 640, 128), (520, 16, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", MX_SHAPES)
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_mxfp4_gemm(orc, M, N, K, bf16_out):
+    _gemm_case(orc, 0, M, N, K, bf16_out, seed=M * 7 + N * 3 + K)
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 255, 640)])
+def test_mxfp4_ocp_gemm(orc, M, N, K):
+    _gemm_case(orc, 2, M, N, K, False, seed=11)
+
+
+def test_mxfp4_256_config_fp32_out(orc):
+    """The 256^3 MXFP4 workload: FP32 A, B with every 512th element x20."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    a, b = synth.mxfp4_256()
+    qa, ra = _quant_both(orc, a, 0)
+    qb, rb = _quant_both(orc, b, 0)
+    say("gemm mxfp4_256")
+    C = to_host(fp4.gemm(qa, qb, out_dtype=torch.float32))
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], 256, 256, 256, 0)
+    assert_gemm_close(orc, C, Cref, T, False, "mxfp4_256")
+
+
+def _pack(c):
+    c = np.asarray(c, np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _scales(orc, fmt, rows, K, byte_of):
+    s = np.zeros(orc.scale_bytes(fmt, rows, K), np.uint8)
+    for r in range(rows):
+        for b in range(K // orc.block_size(fmt)):
+            s[orc.scale_offset(fmt, rows, K, r, b)] = byte_of(r, b)
+    return s
+
+
+def _run_raw(fmt, A, sA, B, sB, M, N, K, tsA=None, tsB=None):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    Cd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dA, dsA, dB, dsB = to_dev(A), to_dev(sA), to_dev(B), to_dev(sB)
+    tA = None if tsA is None else torch.tensor([tsA], dtype=torch.float32, device="cuda")
+    tB = None if tsB is None else torch.tensor([tsB], dtype=torch.float32, device="cuda")
+    ws = fp4.workspace(fp4.OP_GEMM, fmt, M, N, K)
+    rc = fp4.fp4_gemm(dA.data_ptr(), dsA.data_ptr(), dB.data_ptr(), dsB.data_ptr(),
+                      None if tA is None else tA.data_ptr(), None if tB is None else tB.data_ptr(), Cd.data_ptr(),
+                      M, N, K, fmt, fp4.F32, None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+                      torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fp4.fp4_status_string(rc)
+    return to_host(Cd)
+
+
+@pytest.mark.parametrize("fmt", [0])
+def test_closed_forms_bit_exact(orc, fmt):
+    """All-6 operands with unit scales give 36*K; one-hot operands pin the
+    row/column/K and nibble mapping; alternating signs cancel exactly."""
+    M, N, K = 40, 24, 512
+    unit = 127 if fmt != 1 else 0x38
+    s1a = _scales(orc, fmt, M, K, lambda r, b: unit)
+    s1b = _scales(orc, fmt, N, K, lambda r, b: unit)
+    say("closed form all-6")
+    C = _run_raw(fmt, _pack(np.full((M, K), 7)), s1a, _pack(np.full((N, K), 7)), s1b, M, N, K, 1.0, 1.0)
+    np.testing.assert_array_equal(C, np.full((M, N), 36.0 * K, np.float32))
+    alt = np.tile(np.array([7, 15], np.uint8), (N, K // 2))
+    say("closed form alternating")
+    C = _run_raw(fmt, _pack(np.full((M, K), 7)), s1a, _pack(alt), s1b, M, N, K, 1.0, 1.0)
+    np.testing.assert_array_equal(C, np.zeros((M, N), np.float32))
+    g = np.random.default_rng(5)
+    for trial in range(6):
+        m, n, k = int(g.integers(M)), int(g.integers(N)), int(g.integers(K))
+        a1 = np.zeros((M, K), np.uint8)
+        b1 = np.zeros((N, K), np.uint8)
+        ca, cb = int(g.integers(1, 16)), int(g.integers(1, 16))
+        a1[m, k] = ca
+        b1[n, k] = cb
+        ea, eb = int(g.integers(-5, 6)), int(g.integers(-5, 6))
+        sa = _scales(orc, fmt, M, K, lambda r, b: 127 + ea)
+        sb = _scales(orc, fmt, N, K, lambda r, b: 127 + eb)
+        say("closed form one-hot m=%d n=%d k=%d" % (m, n, k))
+        C = _run_raw(fmt, _pack(a1), sa, _pack(b1), sb, M, N, K)
+        ref = np.zeros((M, N), np.float32)
+        ref[m, n] = orc.e2m1_value(ca) * orc.e2m1_value(cb) * 2.0 ** (ea + eb)
+        np.testing.assert_array_equal(C, ref)
+
+
+def test_exact_small_exponent_range_bit_exact(orc):
+    """Scale exponents within a range of 4 and K <= 256 keep every partial sum
+    exact in FP32, so any accumulation order gives the oracle's value."""
+    fmt, M, N, K = 0, 48, 80, 256
+    g = np.random.default_rng(9)
+    A = g.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    B = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sA = _scales(orc, fmt, M, K, lambda r, b: int(125 + g.integers(0, 3)))
+    sB = _scales(orc, fmt, N, K, lambda r, b: int(126 + g.integers(0, 2)))
+    say("exact small range")
+    C = _run_raw(fmt, A, sA, B, sB, M, N, K)
+    Cref, _ = orc.gemm(A, sA, B, sB, M, N, K, fmt)
+    np.testing.assert_array_equal(C.astype(np.float64), Cref)
+
+
+def test_mxfp4_8192_sampled(orc):
+    """The 8192^3 MXFP4 workload in the benchmark's launch configuration; 24
+    sampled rows x 24 sampled columns against the oracle (which quantises just
+    those rows of A and B itself)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    a, b = synth.mxfp4_8192()
+    say("gemm mxfp4_8192 full size")
+    qa = fp4.quantize(to_dev(a), 0)
+    qb = fp4.quantize(to_dev(b), 0)
+    C = fp4.gemm(qa, qb, out_dtype=torch.bfloat16)
+    g = np.random.default_rng(3)
+    rows = np.sort(np.concatenate([[0, 8191], g.choice(8192, 22, replace=False)]))
+    cols = np.sort(np.concatenate([[0, 8191], g.choice(8192, 22, replace=False)]))
+    Cs = to_host(C)[np.ix_(rows, cols)]
+    ra = orc.quantize(a[rows], 0)
+    rb = orc.quantize(b[cols], 0)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 8192, 0)
+    assert_gemm_close(orc, Cs, Cref, T, True, "mxfp4_8192 sampled")
