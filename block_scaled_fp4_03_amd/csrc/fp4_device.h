@@ -79,22 +79,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Byte offset of scale (row r, block b) in the tiled layout of a matrix with
-// KT = ceil(KB/16) block tiles per row tile.
+// Byte offset of scale (row r, block b) in the tiled layout:
+//   MXFP4: 256-byte tiles of 32 rows x 8 blocks; row i, block q of a tile in
+//          lane 32*(q%2) + i, byte q/2 -- the lane order of the 32x32x64
+//          matrix-core operand (lane = 32*chunk + row), one byte per 64-value
+//          K sub-step.
+//   NVFP4: 256-byte tiles of 16 rows x 16 blocks; row i, block q in lane
+//          16*((q/2)%4) + i, byte 2*(q/8) + q%2.
+// KT = number of block tiles per row tile.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_offset(uint32_t r, uint32_t b, uint32_t KT) {
-  uint32_t tile = (r >> 4) * KT + (b >> 4);
-  uint32_t i = r & 15u, q = b & 15u;
-  uint32_t lane, byte;
+  uint32_t lane, byte, tile;
   if (FMT == kFmtNV) {
+    const uint32_t i = r & 15u, q = b & 15u;
+    tile = (r >> 4) * KT + (b >> 4);
     lane = 16u * ((q >> 1) & 3u) + i;
     byte = 2u * (q >> 3) + (q & 1u);
   } else {
-    lane = 16u * (q & 3u) + i;
-    byte = q >> 2;
+    const uint32_t i = r & 31u, q = b & 7u;
+    tile = (r >> 5) * KT + (b >> 3);
+    lane = 32u * (q & 1u) + i;
+    byte = q >> 1;
   }
   return tile * 256u + lane * 4u + byte;
 }
-
 
 }  // namespace fp4

@@ -101,18 +101,19 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 quantiser.  Waves cover rows_pad = 16 * ceil(rows/16) rows so that the
+// MXFP4 quantiser.  One wave covers two 256-element scale tiles (8 blocks
+// each) of one row; waves cover rows_pad = 32 * ceil(rows/32) rows so that the
 // padding rows of the scale tiles are written (as 0).
 // ---------------------------------------------------------------------------
 template <int FMT, int DT>
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, uint32_t rows, uint32_t K,
-                                                          uint32_t KT, uint32_t total_waves) {
+                                                          uint32_t KT, uint32_t KT2, uint32_t total_waves) {
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
   const uint32_t lane = threadIdx.x & 63u;
   if (wave >= total_waves) return;
-  const uint32_t row = wave / KT, kt = wave % KT;
-  const uint32_t k0 = kt * 512u + lane * 8u;
+  const uint32_t row = wave / KT2, kt2 = wave % KT2;
+  const uint32_t k0 = kt2 * 512u + lane * 8u;
   const bool valid = row < rows && k0 < K;
   float v[8];
   if (valid) {
@@ -136,16 +137,18 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
     for (int k = 0; k < 8; ++k) y[k] = v[k] * inv;
     *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
   }
-  // Scale dword for chunk j = lane (lanes 0..3): blocks q = j, 4+j, 8+j, 12+j of
-  // this slice, block q held by lane 4q.
-  const uint32_t j = lane & 3u;
-  const uint32_t b0 = __shfl(sbyte, 4 * j);
-  const uint32_t b1 = __shfl(sbyte, 4 * (4 + j));
-  const uint32_t b2 = __shfl(sbyte, 4 * (8 + j));
-  const uint32_t b3 = __shfl(sbyte, 4 * (12 + j));
-  if (lane < 4u) {
+  // Tile t = lane / 32 holds blocks 8t..8t+7 of the slice (block q of the
+  // slice in lanes 4q..4q+3).  Its dword for chunk j (lanes 32t + j, j < 2)
+  // holds blocks q = j, 2+j, 4+j, 6+j in bytes 0..3.
+  const uint32_t base = lane & 32u, j = lane & 1u;
+  const uint32_t b0 = __shfl(sbyte, base + 4 * j);
+  const uint32_t b1 = __shfl(sbyte, base + 4 * j + 8);
+  const uint32_t b2 = __shfl(sbyte, base + 4 * j + 16);
+  const uint32_t b3 = __shfl(sbyte, base + 4 * j + 24);
+  const uint32_t kt = 2u * kt2 + (lane >> 5);
+  if ((lane & 31u) < 2u && kt < KT) {
     const uint32_t dw = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-    const size_t off = ((size_t)(row >> 4) * KT + kt) * 256u + (16u * j + (row & 15u)) * 4u;
+    const size_t off = ((size_t)(row >> 5) * KT + kt) * 256u + (32u * j + (row & 31u)) * 4u;
     *reinterpret_cast<uint32_t*>(scales + off) = dw;
   }
 }
@@ -284,19 +287,22 @@ hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes,
       quantize_nv_kernel<kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
                                                                   waves);
   } else {
-    const uint32_t KT = (k / 32u + 15u) / 16u;
-    const uint32_t waves = rows_pad * KT;
+    const uint32_t rows_pad32 = (r + 31u) / 32u * 32u;
+    const uint32_t KT = (k / 32u + 7u) / 8u, KT2 = (KT + 1u) / 2u;
+    const uint32_t waves = rows_pad32 * KT2;
     const dim3 grid((waves + 3u) / 4u);
     if (fmt == kFmtMX) {
       if (in_dtype == kDtF32)
-        quantize_mx_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+        quantize_mx_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves);
       else
-        quantize_mx_kernel<kFmtMX, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+        quantize_mx_kernel<kFmtMX, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves);
     } else {
       if (in_dtype == kDtF32)
-        quantize_mx_kernel<kFmtMXOcp, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+        quantize_mx_kernel<kFmtMXOcp, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2,
+                                                                              waves);
       else
-        quantize_mx_kernel<kFmtMXOcp, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, waves);
+        quantize_mx_kernel<kFmtMXOcp, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2,
+                                                                               waves);
     }
   }
   return hipGetLastError();
@@ -314,7 +320,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
     else
       dequantize_kernel<kFmtNV, kDtBF16><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
   } else {
-    const uint32_t KT = (k / 32u + 15u) / 16u;
+    const uint32_t KT = (k / 32u + 7u) / 8u;
     if (out_dtype == kDtF32)
       dequantize_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
     else

@@ -196,38 +196,38 @@ uint16_t oracle_f32_to_bf16(float f)
 
 /* ------------------------------------------------------------------ */
 /* Scale-buffer layout (the library's documented byte order).  Scales
- * live in tiles of 16 rows x 16 blocks = 256 bytes, tiles row-major over
- * (row tile, block tile).  Inside a tile the byte of (row i, block q) is
- * at 4*lane + byte with lane = 16*j + i, where j is the 32-element K
- * chunk of a 128-element K step that holds the block:
- *   MXFP4 (32-blocks): q = 4*s + j,           byte = s    (s = step 0..3)
- *   NVFP4 (16-blocks): q = 8*h + 2*j + t,     byte = 2*h + t
+ * live in 256-byte tiles stored row-tile major; inside a tile the 256
+ * bytes are 64 dwords ("lanes").
+ *   MXFP4 (32-blocks): tiles of 32 rows x 8 blocks.  Row i, block q of a
+ *     tile sit in lane 32*(q%2) + i, byte q/2.
+ *   NVFP4 (16-blocks): tiles of 16 rows x 16 blocks.  Row i, block q sit
+ *     in lane 16*((q/2)%4) + i, byte 2*(q/8) + q%2.
  * Padding rows and blocks hold 0.                                      */
 /* ------------------------------------------------------------------ */
 static int64_t block_size(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 32; }
+static int64_t tile_rows(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 32; }
+static int64_t tile_blocks(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 8; }
 
 int64_t oracle_scale_bytes(int fmt, int64_t rows, int64_t K)
 {
-    int64_t KB = K / block_size(fmt);
-    return ((rows + 15) / 16) * ((KB + 15) / 16) * 256;
+    int64_t KB = K / block_size(fmt), TR = tile_rows(fmt), TB = tile_blocks(fmt);
+    return ((rows + TR - 1) / TR) * ((KB + TB - 1) / TB) * 256;
 }
 
 int64_t oracle_scale_offset(int fmt, int64_t rows, int64_t K, int64_t r, int64_t b)
 {
     (void)rows;
-    int64_t KB = K / block_size(fmt);
-    int64_t KT = (KB + 15) / 16;
-    int64_t tile = (r / 16) * KT + b / 16;
-    int64_t i = r % 16, q = b % 16;
+    int64_t KB = K / block_size(fmt), TR = tile_rows(fmt), TB = tile_blocks(fmt);
+    int64_t KT = (KB + TB - 1) / TB;
+    int64_t tile = (r / TR) * KT + b / TB;
+    int64_t i = r % TR, q = b % TB;
     int64_t lane, byte;
     if (fmt == OR_FMT_NVFP4) {
-        int64_t h = q / 8, j = (q / 2) % 4, t = q % 2;
-        lane = 16 * j + i;
-        byte = 2 * h + t;
+        lane = 16 * ((q / 2) % 4) + i;
+        byte = 2 * (q / 8) + q % 2;
     } else {
-        int64_t s = q / 4, j = q % 4;
-        lane = 16 * j + i;
-        byte = s;
+        lane = 32 * (q % 2) + i;
+        byte = q / 2;
     }
     return tile * 256 + lane * 4 + byte;
 }
