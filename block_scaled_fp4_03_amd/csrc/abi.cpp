@@ -31,10 +31,8 @@ extern "C" {
 int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K) {
   if (!fmt_ok(fmt)) return FP4_ERR_FMT;
   if (rows < 0 || K < 0 || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
-  const int64_t KB = K / block_of(fmt);
-  // MXFP4 tiles: 32 rows x 8 blocks; NVFP4 tiles: 16 rows x 16 blocks (256 B each).
-  const int64_t tr = fmt == FP4_NVFP4 ? 16 : 32, tb = fmt == FP4_NVFP4 ? 16 : 8;
-  return ((rows + tr - 1) / tr) * ((KB + tb - 1) / tb) * 256;
+  // Tiles of 32 rows x 256 K values: 256 bytes (MXFP4) or 512 bytes (NVFP4).
+  return ((rows + 31) / 32) * ((K + 255) / 256) * (fmt == FP4_NVFP4 ? 512 : 256);
 }
 
 size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E) {

@@ -79,29 +79,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Byte offset of scale (row r, block b) in the tiled layout:
-//   MXFP4: 256-byte tiles of 32 rows x 8 blocks; row i, block q of a tile in
-//          lane 32*(q%2) + i, byte q/2 -- the lane order of the 32x32x64
-//          matrix-core operand (lane = 32*chunk + row), one byte per 64-value
-//          K sub-step.
-//   NVFP4: 256-byte tiles of 16 rows x 16 blocks; row i, block q in lane
-//          16*((q/2)%4) + i, byte 2*(q/8) + q%2.
-// KT = number of block tiles per row tile.
+// Byte offset of scale (row r, block b) in the tiled layout.  Tiles cover
+// 32 rows x 256 K values and are stored row-tile major (KT tiles per row
+// tile); inside a tile, row i and 32-value K chunk c (0..7) belong to lane
+// 32*(c%2) + i of the 32x32 matrix-core operand, sub-step s = c/2:
+//   MXFP4: 256-byte tiles, lane L's 4 bytes at 4L, byte s = chunk's block;
+//   NVFP4: 512-byte tiles, lane L's 8 bytes at 8L, bytes 2s, 2s+1 = the
+//          chunk's two 16-blocks.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_offset(uint32_t r, uint32_t b, uint32_t KT) {
-  uint32_t lane, byte, tile;
-  if (FMT == kFmtNV) {
-    const uint32_t i = r & 15u, q = b & 15u;
-    tile = (r >> 4) * KT + (b >> 4);
-    lane = 16u * ((q >> 1) & 3u) + i;
-    byte = 2u * (q >> 3) + (q & 1u);
-  } else {
-    const uint32_t i = r & 31u, q = b & 7u;
-    tile = (r >> 5) * KT + (b >> 3);
-    lane = 32u * (q & 1u) + i;
-    byte = q >> 1;
-  }
-  return tile * 256u + lane * 4u + byte;
+  const uint32_t k0 = (FMT == kFmtNV) ? 16u * b : 32u * b;
+  const uint32_t tile = (r >> 5) * KT + (k0 >> 8);
+  const uint32_t i = r & 31u, c = (k0 & 255u) >> 5;
+  const uint32_t lane = 32u * (c & 1u) + i, s = c >> 1;
+  if (FMT == kFmtNV) return tile * 512u + lane * 8u + 2u * s + (b & 1u);
+  return tile * 256u + lane * 4u + s;
 }
 
 }  // namespace fp4

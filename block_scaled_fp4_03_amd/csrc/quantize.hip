@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
 
 // ---------------------------------------------------------------------------
 // NVFP4 quantiser.  One wave covers two 256-element scale tiles of one row
-// (lanes 0-31 the first, 32-63 the second).
+// (lanes 0-31 the first, 32-63 the second); waves cover 32 * ceil(rows/32)
+// rows so the tiles' padding rows are written (as 0).
 //   r = (amax_b / 6) / s_t; sb = E4M3(r); d = E4M3value(sb) * s_t;
 //   code = E2M1(x / d)   (x / inf = +-0 when sb == 0, so the block is all zero)
 // All divisions are IEEE FP32 round-to-nearest-even.
@@ -193,17 +194,19 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
     for (int k = 0; k < 8; ++k) y[k] = v[k] / d;
     *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
   }
-  // Tile t = lane / 32; dword for chunk j (lanes 32t + j, j < 4) holds blocks
-  // q = 2j, 2j+1, 8+2j, 9+2j of the tile; block q sits in lane 32t + 2q.
-  const uint32_t base = lane & 32u, j = lane & 3u;
-  const uint32_t c0 = __shfl(sb, base + 4 * j);
-  const uint32_t c1 = __shfl(sb, base + 4 * j + 2);
-  const uint32_t c2 = __shfl(sb, base + 16 + 4 * j);
-  const uint32_t c3 = __shfl(sb, base + 18 + 4 * j);
+  // Tile T = lane / 32 holds blocks q = 0..15 of 16 values (block q in lanes
+  // 32T + 2q, 32T + 2q + 1).  Tile lane 32j + i (j = chunk parity) holds 8
+  // bytes: dword d has blocks 8d + 2j + {0, 1, 4, 5}.  Writer lane 32T + 2j + d.
+  const uint32_t base = lane & 32u, j = (lane >> 1) & 1u, d = lane & 1u;
+  const uint32_t q0 = 8u * d + 2u * j;
+  const uint32_t c0 = __shfl(sb, base + 2u * q0);
+  const uint32_t c1 = __shfl(sb, base + 2u * (q0 + 1u));
+  const uint32_t c2 = __shfl(sb, base + 2u * (q0 + 4u));
+  const uint32_t c3 = __shfl(sb, base + 2u * (q0 + 5u));
   const uint32_t kt = 2u * kt2 + (lane >> 5);
   if ((lane & 31u) < 4u && kt < KT) {
     const uint32_t dw = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    const size_t off = ((size_t)(row >> 4) * KT + kt) * 256u + (16u * j + (row & 15u)) * 4u;
+    const size_t off = ((size_t)(row >> 5) * KT + kt) * 512u + (32u * j + (row & 31u)) * 8u + 4u * d;
     *reinterpret_cast<uint32_t*>(scales + off) = dw;
   }
 }
@@ -275,9 +278,9 @@ hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* 
 hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
                            const float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream) {
   const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
-  const uint32_t rows_pad = (r + 15u) / 16u * 16u;
+  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
   if (fmt == kFmtNV) {
-    const uint32_t KT = (k / 16u + 15u) / 16u, KT2 = (KT + 1u) / 2u;
+    const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
     const uint32_t waves = rows_pad * KT2;
     const dim3 grid((waves + 3u) / 4u);
     if (in_dtype == kDtF32)
@@ -287,9 +290,8 @@ hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes,
       quantize_nv_kernel<kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
                                                                   waves);
   } else {
-    const uint32_t rows_pad32 = (r + 31u) / 32u * 32u;
-    const uint32_t KT = (k / 32u + 7u) / 8u, KT2 = (KT + 1u) / 2u;
-    const uint32_t waves = rows_pad32 * KT2;
+    const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
+    const uint32_t waves = rows_pad * KT2;
     const dim3 grid((waves + 3u) / 4u);
     if (fmt == kFmtMX) {
       if (in_dtype == kDtF32)
@@ -313,14 +315,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
   const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
   const size_t threads = (size_t)r * (k / 8u);
   const dim3 grid((unsigned)((threads + 255) / 256));
+  const uint32_t KT = (k + 255u) / 256u;
   if (fmt == kFmtNV) {
-    const uint32_t KT = (k / 16u + 15u) / 16u;
     if (out_dtype == kDtF32)
       dequantize_kernel<kFmtNV, kDtF32><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
     else
       dequantize_kernel<kFmtNV, kDtBF16><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
   } else {
-    const uint32_t KT = (k / 32u + 7u) / 8u;
     if (out_dtype == kDtF32)
       dequantize_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(codes, scales, tensor_scale, out, r, k, KT);
     else

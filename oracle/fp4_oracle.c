@@ -196,40 +196,36 @@ uint16_t oracle_f32_to_bf16(float f)
 
 /* ------------------------------------------------------------------ */
 /* Scale-buffer layout (the library's documented byte order).  Scales
- * live in 256-byte tiles stored row-tile major; inside a tile the 256
- * bytes are 64 dwords ("lanes").
- *   MXFP4 (32-blocks): tiles of 32 rows x 8 blocks.  Row i, block q of a
- *     tile sit in lane 32*(q%2) + i, byte q/2.
- *   NVFP4 (16-blocks): tiles of 16 rows x 16 blocks.  Row i, block q sit
- *     in lane 16*((q/2)%4) + i, byte 2*(q/8) + q%2.
+ * live in tiles of 32 rows x 256 K values, stored row-tile major; inside
+ * a tile, row i and 32-value K chunk c (c = 0..7) belong to "lane"
+ * 32*(c%2) + i and "sub-step" c/2.
+ *   MXFP4 (32-blocks): 256-byte tiles; lane L holds 4 bytes at 4L, byte
+ *     s = the sub-step's block (block q = chunk q).
+ *   NVFP4 (16-blocks): 512-byte tiles; lane L holds 8 bytes at 8L, bytes
+ *     2s and 2s+1 = the sub-step chunk's two blocks (block q is in chunk
+ *     q/2, half q%2).
  * Padding rows and blocks hold 0.                                      */
 /* ------------------------------------------------------------------ */
 static int64_t block_size(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 32; }
-static int64_t tile_rows(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 32; }
-static int64_t tile_blocks(int fmt) { return fmt == OR_FMT_NVFP4 ? 16 : 8; }
+static int64_t tile_bytes(int fmt) { return fmt == OR_FMT_NVFP4 ? 512 : 256; }
 
 int64_t oracle_scale_bytes(int fmt, int64_t rows, int64_t K)
 {
-    int64_t KB = K / block_size(fmt), TR = tile_rows(fmt), TB = tile_blocks(fmt);
-    return ((rows + TR - 1) / TR) * ((KB + TB - 1) / TB) * 256;
+    int64_t KT = (K + 255) / 256;
+    return ((rows + 31) / 32) * KT * tile_bytes(fmt);
 }
 
 int64_t oracle_scale_offset(int fmt, int64_t rows, int64_t K, int64_t r, int64_t b)
 {
     (void)rows;
-    int64_t KB = K / block_size(fmt), TR = tile_rows(fmt), TB = tile_blocks(fmt);
-    int64_t KT = (KB + TB - 1) / TB;
-    int64_t tile = (r / TR) * KT + b / TB;
-    int64_t i = r % TR, q = b % TB;
-    int64_t lane, byte;
-    if (fmt == OR_FMT_NVFP4) {
-        lane = 16 * ((q / 2) % 4) + i;
-        byte = 2 * (q / 8) + q % 2;
-    } else {
-        lane = 32 * (q % 2) + i;
-        byte = q / 2;
-    }
-    return tile * 256 + lane * 4 + byte;
+    int64_t KT = (K + 255) / 256;
+    int64_t k0 = b * block_size(fmt);          /* first K value of the block */
+    int64_t tile = (r / 32) * KT + k0 / 256;
+    int64_t i = r % 32, c = (k0 % 256) / 32;    /* row and chunk in the tile */
+    int64_t lane = 32 * (c % 2) + i, s = c / 2;
+    if (fmt == OR_FMT_NVFP4)
+        return tile * 512 + lane * 8 + 2 * s + (b % 2);
+    return tile * 256 + lane * 4 + s;
 }
 
 /* ------------------------------------------------------------------ */

@@ -42,11 +42,11 @@ def test_status_strings(L):
 
 def test_scale_bytes(L):
     assert fp4.fp4_scale_bytes(fp4.MXFP4, 256, 256) == 8 * 1 * 256
-    assert fp4.fp4_scale_bytes(fp4.NVFP4, 8192, 8192) == 512 * 32 * 256
+    assert fp4.fp4_scale_bytes(fp4.NVFP4, 8192, 8192) == 256 * 32 * 512
     assert fp4.fp4_scale_bytes(fp4.MXFP4, 5760, 2880) == 180 * 12 * 256
     assert fp4.fp4_scale_bytes(fp4.MXFP4, 17, 96) == 1 * 1 * 256
     assert fp4.fp4_scale_bytes(fp4.MXFP4, 4, 48) == -2  # K % 32
-    assert fp4.fp4_scale_bytes(fp4.NVFP4, 4, 48) == 256
+    assert fp4.fp4_scale_bytes(fp4.NVFP4, 4, 48) == 512
     assert fp4.fp4_scale_bytes(7, 4, 64) == -4
     assert fp4.fp4_scale_bytes(fp4.MXFP4, -1, 64) == -2
 

@@ -157,8 +157,7 @@ def test_scale_layout_is_a_bijection(orc, fmt, rows, K):
         pytest.skip("shape not defined for this block size")
     KB = K // bs
     total = orc.scale_bytes(fmt, rows, K)
-    tr, tb = (16, 16) if fmt == 1 else (32, 8)
-    assert total == ((rows + tr - 1) // tr) * ((KB + tb - 1) // tb) * 256
+    assert total == ((rows + 31) // 32) * ((K + 255) // 256) * (512 if fmt == 1 else 256)
     offs = np.array([orc.scale_offset(fmt, rows, K, r, b) for r in range(rows) for b in range(KB)])
     assert offs.min() >= 0 and offs.max() < total
     assert np.unique(offs).size == offs.size

@@ -48,6 +48,33 @@ def test_mxfp4_ocp_gemm(orc, M, N, K):
     _gemm_case(orc, 2, M, N, K, False, seed=11)
 
 
+NV_SHAPES = [(256, 256, 256), (1, 1, 32), (17, 33, 96), (300, 260, 544), (512, 512, 1024), (257, 513, 2880),
+             (64, 640, 128), (520, 16, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", NV_SHAPES)
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_nvfp4_gemm(orc, M, N, K, bf16_out):
+    _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 5 + N * 11 + K, a_std=3.0, b_std=0.05)
+
+
+def test_nvfp4_gemm_row_scaled(orc):
+    """Rows with standard deviations spread log-uniformly over [0.01, 1] (the
+    MLP workload's law), BF16 activations quantised on the GPU."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    M, N, K = 384, 320, 1024
+    a = synth.to_bf16_bits(synth.row_scaled_gaussian(61, M, K))
+    w = synth.row_scaled_gaussian(62, N, K)
+    say("gemm nvfp4 row-scaled")
+    qa, ra = _quant_both(orc, a, 1)
+    qb, rb = _quant_both(orc, w, 1)
+    assert to_host(qa.tensor_scale)[0] == np.float32(ra[3])
+    C = fp4.gemm(qa, qb, out_dtype=torch.bfloat16)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, 1, tsA=ra[3], tsB=rb[3])
+    assert_gemm_close(orc, to_host(C), Cref, T, True, "nvfp4 row-scaled")
+
+
 def test_mxfp4_256_config_fp32_out(orc):
     """The 256^3 MXFP4 workload: FP32 A, B with every 512th element x20."""
     import block_scaled_fp4_03_amd as fp4
@@ -90,7 +117,7 @@ def _run_raw(fmt, A, sA, B, sB, M, N, K, tsA=None, tsB=None):
     return to_host(Cd)
 
 
-@pytest.mark.parametrize("fmt", [0])
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_closed_forms_bit_exact(orc, fmt):
     """All-6 operands with unit scales give 36*K; one-hot operands pin the
     row/column/K and nibble mapping; alternating signs cancel exactly."""
@@ -113,13 +140,20 @@ def test_closed_forms_bit_exact(orc, fmt):
         ca, cb = int(g.integers(1, 16)), int(g.integers(1, 16))
         a1[m, k] = ca
         b1[n, k] = cb
-        ea, eb = int(g.integers(-5, 6)), int(g.integers(-5, 6))
-        sa = _scales(orc, fmt, M, K, lambda r, b: 127 + ea)
-        sb = _scales(orc, fmt, N, K, lambda r, b: 127 + eb)
+        if fmt == 1:  # E4M3 scales, any byte (normal or subnormal)
+            ea, eb = int(g.integers(1, 127)), int(g.integers(1, 127))
+            sa = _scales(orc, fmt, M, K, lambda r, b: ea)
+            sb = _scales(orc, fmt, N, K, lambda r, b: eb)
+            want = orc.e2m1_value(ca) * orc.e2m1_value(cb) * orc.e4m3_value(ea) * orc.e4m3_value(eb)
+        else:
+            ea, eb = int(g.integers(-5, 6)), int(g.integers(-5, 6))
+            sa = _scales(orc, fmt, M, K, lambda r, b: 127 + ea)
+            sb = _scales(orc, fmt, N, K, lambda r, b: 127 + eb)
+            want = orc.e2m1_value(ca) * orc.e2m1_value(cb) * 2.0 ** (ea + eb)
         say("closed form one-hot m=%d n=%d k=%d" % (m, n, k))
-        C = _run_raw(fmt, _pack(a1), sa, _pack(b1), sb, M, N, K)
+        C = _run_raw(fmt, _pack(a1), sa, _pack(b1), sb, M, N, K, 1.0, 1.0)
         ref = np.zeros((M, N), np.float32)
-        ref[m, n] = orc.e2m1_value(ca) * orc.e2m1_value(cb) * 2.0 ** (ea + eb)
+        ref[m, n] = want
         np.testing.assert_array_equal(C, ref)
 
 
@@ -157,3 +191,28 @@ def test_mxfp4_8192_sampled(orc):
     rb = orc.quantize(b[cols], 0)
     Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 8192, 0)
     assert_gemm_close(orc, Cs, Cref, T, True, "mxfp4_8192 sampled")
+
+
+def test_nvfp4_mlp_sampled(orc):
+    """The 4096 x 14336 x 4096 NVFP4 workload (BF16 activations quantised on
+    the fly, weights pre-quantised) in the benchmark's launch configuration;
+    24 x 24 sampled outputs against the oracle, which quantises those rows
+    itself with the tensor scales it computes from the whole operands."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    a, w = synth.nvfp4_mlp()
+    say("gemm nvfp4_mlp full size")
+    qa = fp4.quantize(to_dev(a), 1)
+    qw = fp4.quantize(to_dev(w), 1)
+    C = fp4.gemm(qa, qw, out_dtype=torch.bfloat16)
+    g = np.random.default_rng(4)
+    rows = np.sort(np.concatenate([[0, 4095], g.choice(4096, 22, replace=False)]))
+    cols = np.sort(np.concatenate([[0, 14335], g.choice(14336, 22, replace=False)]))
+    Cs = to_host(C)[np.ix_(rows, cols)]
+    ts_a = orc.nvfp4_tensor_scale(orc.tensor_amax(a))
+    ts_w = orc.nvfp4_tensor_scale(orc.tensor_amax(w))
+    assert to_host(qa.tensor_scale)[0] == np.float32(ts_a) and to_host(qw.tensor_scale)[0] == np.float32(ts_w)
+    ra = orc.quantize(a[rows], 1, tensor_scale=ts_a)
+    rb = orc.quantize(w[cols], 1, tensor_scale=ts_w)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 4096, 1, tsA=ts_a, tsB=ts_w)
+    assert_gemm_close(orc, Cs, Cref, T, True, "nvfp4_mlp sampled")
