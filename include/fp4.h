@@ -36,18 +36,22 @@
  *                    NVFP4  E2M1(code) * E4M3(scale_byte) * tensor_scale.
  *
  * Tiled scale layout (identical for A and B operands; both are "rows x K").
- *   A row has KB = K / bs blocks (bs = 32 for MXFP4, 16 for NVFP4).  Scales are
- *   grouped in tiles of 16 rows x 16 blocks, 256 bytes each, stored row-tile
- *   major: tile (rt, kt) starts at byte 256 * (rt * ceil(KB/16) + kt).  Inside
- *   a tile, view the 256 bytes as 64 dwords ("lanes"); the block of row
- *   16*rt + i that covers 32-value chunk j (j = 0..3) of a 128-value K step
- *   sits in lane 16*j + i, and the byte within the lane is:
- *     MXFP4: the K step s = 0..3 within the tile   (block q = 4*s + j)
- *     NVFP4: 2*h + t, h = K step 0..1 within the tile, t = first or second
- *            16-block of the 32-value chunk          (block q = 8*h + 2*j + t)
- *   so one dword load per lane yields the scales one wavefront needs for four
- *   (MXFP4) or two (NVFP4) K steps of a 16-row matrix-core operand.  Bytes of
- *   rows >= `rows` or blocks >= KB are padding; the quantiser writes them as 0.
+ *   Scales are grouped in tiles of 32 rows x 256 K values, stored row-tile
+ *   major: tile (rt, kt) starts at byte T * (rt * ceil(K/256) + kt), with tile
+ *   size T = 256 (MXFP4: 8 blocks of 32) or 512 (NVFP4: 16 blocks of 16).
+ *   Inside a tile, row i (0..31) and 32-value K chunk c (0..7) belong to lane
+ *   L = 32 * (c % 2) + i and sub-step s = c / 2 -- the lane order of the 32x32
+ *   matrix-core operand, where lane 32*j + i carries row i's chunk j of each
+ *   64-value K sub-step:
+ *     MXFP4: lane L owns bytes 4L..4L+3; byte 4L + s is the chunk's E8M0 scale;
+ *     NVFP4: lane L owns bytes 8L..8L+7; bytes 8L + 2s and 8L + 2s + 1 are the
+ *            E4M3 scales of the chunk's first and second 16-value block.
+ *   One dword (MXFP4) or two (NVFP4) per lane thus carry a wavefront's scales
+ *   for four K sub-steps.  Bytes of rows >= `rows` or of blocks past K are
+ *   padding: the quantiser writes them as 0, and the GEMMs rely on that (a
+ *   zero scale makes the codes read past the end of K contribute nothing), so
+ *   hand-built scale buffers must keep padding bytes 0.  E8M0 byte 0xFF (NaN)
+ *   is never produced and not supported as input.
  */
 #ifndef FP4_H_
 #define FP4_H_
@@ -93,10 +97,13 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
 
 /* Workspace bytes an operation needs (0 if none).  For FP4_OP_QUANTIZE, M is
  * the row count; for FP4_OP_GEMM_GROUPED, E is the expert count and M the total
- * routed rows.  A workspace must be zero-filled once before its first use; every
- * call leaves it zero-filled again when its work on the stream completes.
- * Calls that share one workspace must be ordered (same stream, or events).
- * Host-only. */
+ * routed rows.  Operations keep their control words (completion counters) at
+ * the start of the workspace and scratch data after them.  A workspace must be
+ * zero-filled once before its first use; every call leaves the control words
+ * zero again when its work on the stream completes, so one zero-filled
+ * workspace of the largest size needed serves any sequence of calls.  Calls
+ * that share one workspace must be ordered (same stream, or events); calls
+ * that overlap on one workspace race.  Host-only. */
 size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E);
 
 /* Quantise a rows x K matrix x (K contiguous) of `in_dtype` (FP32 or BF16).
@@ -110,9 +117,8 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
  *   s_t >= FLT_MIN, and written to *tensor_scale.  With FP4_TS_GIVEN the caller's
  *   value is used (it must be a positive, finite, normal FP32).
  *   (Sources: glossary "How FP4 works"; NVFP4 video transcript.)
- * Requirements: K % bs == 0; x 16-byte aligned and K*elem_size % 16 == 0;
- *   codes 16-byte aligned with K % 32 == 0 (so rows are whole 16-byte units);
- *   block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
+ * Requirements: K % bs == 0 (32 for MXFP4, 16 for NVFP4); x 16-byte aligned;
+ *   codes and block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
  *   is ignored for MXFP4.  NVFP4 without FP4_TS_GIVEN needs a workspace of
  *   fp4_workspace_size(FP4_OP_QUANTIZE, ...) bytes; otherwise workspace may be NULL.
  * rows == 0 or K == 0 is a no-op. */
@@ -135,9 +141,12 @@ int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const floa
  *   MXFP4 runs on the gfx950 block-scaled FP4 matrix core with the E8M0 scales
  *   applied inside the instruction; NVFP4 decodes E2M1 * E4M3 exactly to FP16
  *   and runs the FP16 matrix core, with the tensor scales in the epilogue.
+ *   NVFP4 with M <= 32 (decode shapes) takes a bandwidth-first path that splits
+ *   K across workgroups and needs the workspace for its partial sums.
  * Requirements: K % 32 == 0 (both formats); codes 16-byte aligned; scales
  *   4-byte aligned; C aligned to its element size.  M, N >= 0 arbitrary.
- *   workspace: fp4_workspace_size(FP4_OP_GEMM, ...) bytes (may be 0 -> NULL ok).
+ *   workspace: fp4_workspace_size(FP4_OP_GEMM, fmt, M, N, K, 0) bytes,
+ *   zero-filled before first use (0 bytes -> NULL is fine).
  * M == 0 or N == 0 is a no-op; K == 0 writes zeros. */
 int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* tsA,
              const float* tsB, void* C, int64_t M, int64_t N, int64_t K, int fmt, int out_dtype,

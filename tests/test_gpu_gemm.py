@@ -216,3 +216,53 @@ def test_nvfp4_mlp_sampled(orc):
     rb = orc.quantize(w[cols], 1, tensor_scale=ts_w)
     Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 4096, 1, tsA=ts_a, tsB=ts_w)
     assert_gemm_close(orc, Cs, Cref, T, True, "nvfp4_mlp sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (17, 256, 4096), (32, 130, 8192),
+                                   (1, 8192, 256), (32, 64, 96)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_nvfp4_decode_gemv(orc, M, N, K, bf16_out):
+    """M <= 32 rows take the decode kernel (split-K partials, last-workgroup
+    reduction); checked in full against the oracle."""
+    _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 13 + N + K, a_std=1.0, b_std=0.02)
+
+
+def test_nvfp4_decode_gemv_repeated_calls(orc):
+    """The split-K counters reset themselves: the same workspace serves
+    several calls in a row (and a smaller problem after a larger one)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    K = 2048
+    w = synth.gaussian(71, (1024, K), std=0.02, bernoulli=0.001)
+    qw, rw = _quant_both(orc, w, 1)
+    ws = torch.zeros(fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 1024, K), dtype=torch.uint8, device="cuda")
+    for M in (32, 8, 1, 32):
+        x = synth.to_bf16_bits(synth.gaussian(72 + M, (M, K)))
+        qx, rx = _quant_both(orc, x, 1)
+        say("gemv repeated M=%d" % M)
+        C = fp4.gemm(qx, qw, out_dtype=torch.float32, ws=ws)
+        Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, 1024, K, 1, tsA=rx[3], tsB=rw[3])
+        assert_gemm_close(orc, to_host(C), Cref, T, False, "gemv repeated M=%d" % M)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_nvfp4_decode_8192_sampled(orc, M):
+    """The decode workload: W 8192 x 8192 N(0, 0.02^2) with 0.1% outliers x20
+    (NVFP4, pre-quantised), X M x 8192 BF16 N(0,1) quantised on the fly; all
+    rows x 48 sampled columns against the oracle."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    w = synth.nvfp4_decode_weight()
+    x = synth.nvfp4_decode_act(M)
+    say("decode 8192 M=%d" % M)
+    qw = fp4.quantize(to_dev(w), 1)
+    qx = fp4.quantize(to_dev(x), 1)
+    C = to_host(fp4.gemm(qx, qw, out_dtype=torch.bfloat16))
+    g = np.random.default_rng(M)
+    cols = np.sort(np.concatenate([[0, 8191], g.choice(8192, 46, replace=False)]))
+    ts_w = orc.nvfp4_tensor_scale(orc.tensor_amax(w))
+    rx = orc.quantize(x, 1)
+    rw = orc.quantize(w[cols], 1, tensor_scale=ts_w)
+    assert to_host(qw.tensor_scale)[0] == np.float32(ts_w)
+    Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, cols.size, 8192, 1, tsA=rx[3], tsB=ts_w)
+    assert_gemm_close(orc, C[:, cols], Cref, T, True, "decode M=%d" % M)
