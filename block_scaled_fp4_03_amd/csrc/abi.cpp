@@ -40,7 +40,7 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
     case FP4_OP_QUANTIZE:
       return fmt == FP4_NVFP4 ? 8 : 0;
     case FP4_OP_GEMM:
-      return fmt == FP4_NVFP4 ? fp4::gemm_nv_workspace(M, N, K) : 0;
+      return (fmt == FP4_NVFP4 && fp4::gemv_nv_applies(M, N)) ? fp4::gemv_nv_workspace(M, N, K) : 0;
     case FP4_OP_GEMM_GROUPED:
       return fp4::gemm_grouped_workspace(M, N, K, E);
     default:
@@ -105,20 +105,20 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
   if (!aligned(tsA, 4) || !aligned(tsB, 4)) return FP4_ERR_ALIGN;
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
-  if (nv) {
-    const size_t need = fp4::gemm_nv_workspace(M, N, K);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return FP4_ERR_ALIGN;
-    return launched(fp4::launch_gemm_nv(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, workspace, workspace_bytes, s));
+  if (nv && fp4::gemv_nv_applies(M, N)) {
+    const size_t need = fp4::gemv_nv_workspace(M, N, K);
+    if (!workspace || workspace_bytes < need) return FP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP4_ERR_ALIGN;
+    return launched(fp4::launch_gemv_nv(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, workspace, s));
   }
-  return launched(fp4::launch_gemm_mx(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
+  return launched(fp4::launch_gemm_tiled(fmt, A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
 }
 
 int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                      const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB, const float* tsA,
                      const float* tsB, void* C, int64_t total_rows, int64_t N, int64_t K, int fmt, int out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!fmt_ok(fmt)) return FP4_ERR_FMT;
+  if (!fmt_ok(fmt) || !fp4::gemm_grouped_supports(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
   if (E < 0 || A_rows < 0 || total_rows < 0 || N < 0 || K < 0 || A_rows > kMaxDim || total_rows > kMaxDim ||
       N > kMaxDim || K > kMaxGemmK || K % 32 != 0)

@@ -20,6 +20,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFmtMX = 0, kFmtNV = 1, kFmtMXOcp = 2;
 
@@ -94,6 +95,36 @@ __device__ __forceinline__ uint32_t scale_offset(uint32_t r, uint32_t b, uint32_
   const uint32_t lane = 32u * (c & 1u) + i, s = c >> 1;
   if (FMT == kFmtNV) return tile * 512u + lane * 8u + 2u * s + (b & 1u);
   return tile * 256u + lane * 4u + s;
+}
+
+
+// ---- NVFP4 operand decode to FP16 (exact: E2M1 x E4M3 needs <= 6 significant
+// bits and lies in [2^-10, 2688]).
+
+// E4M3 byte (0..0x7E) -> FP16 bits.  Normal values (byte >= 8) keep their
+// 3 mantissa bits and rebias the exponent by 8; subnormals m * 2^-9 are normal
+// FP16 numbers and are converted through FP32.
+__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
+  if (b >= 8u) return (b << 7) + 0x2000u;
+  const _Float16 h = (_Float16)((float)b * 0.001953125f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// Both halves of a packed FP16 pair set to the E4M3 scale `b`.
+__device__ __forceinline__ v2h scale_pair(uint32_t b) {
+  const uint32_t h = e4m3_to_f16_bits(b);
+  return __builtin_bit_cast(v2h, h | (h << 16));
+}
+
+// Eight FP16 values = E2M1 codes of one dword (low nibble first) times s.
+// The gfx950 converter gives each code's E2M1 value (scale operand 1.0); the
+// packed multiply by the E4M3 scale is exact.
+__device__ __forceinline__ v8h decode8(uint32_t w, v2h s) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 }  // namespace fp4

@@ -16,22 +16,25 @@ hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes,
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
                              void* out, int out_dtype, int64_t rows, int64_t K, hipStream_t stream);
 
-// MXFP4 GEMM on the block-scaled FP4 matrix core (gemm_mx.hip).
-hipError_t launch_gemm_mx(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                          const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
-                          int out_dtype, hipStream_t stream);
+// Tiled GEMM, MXFP4 (block-scaled FP4 matrix core) or NVFP4 (exact FP16
+// decode) (gemm.hip).
+hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                             const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, hipStream_t stream);
 
-// NVFP4 GEMM / GEMV on the FP16 matrix core after exact decode (gemm_nv.hip).
-hipError_t launch_gemm_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
-                          const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
-                          int out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
-size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K);
-
-// Grouped MXFP4/NVFP4 GEMM (grouped.hip).
+// Grouped (mixture-of-experts) GEMM over the same tiles (gemm.hip).
+bool gemm_grouped_supports(int fmt);
+size_t gemm_grouped_workspace(int64_t total_rows, int64_t N, int64_t K, int32_t E);
 hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                                const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
                                const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N,
                                int64_t K, int fmt, int out_dtype, void* workspace, hipStream_t stream);
-size_t gemm_grouped_workspace(int64_t total_rows, int64_t N, int64_t K, int32_t E);
+
+// NVFP4 decode GEMV / skinny GEMM for M <= 32 (gemv_nv.hip).
+bool gemv_nv_applies(int64_t M, int64_t N);
+size_t gemv_nv_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                          const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                          int out_dtype, void* workspace, hipStream_t stream);
 
 }  // namespace fp4

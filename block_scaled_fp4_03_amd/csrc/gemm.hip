@@ -1,0 +1,443 @@
+// gemm.hip -- tiled FP4 block-scaled GEMM for gfx950: MXFP4 and NVFP4, dense
+// and grouped (mixture-of-experts).
+//
+// C[m,n] = (sum_k A^[m,k] B^[n,k]) * tsA * tsB, A^ and B^ the block-scaled
+// E2M1 operands, FP32 accumulation ("Rubin FP4 GEMM deep dive", §1.1: FP4
+// inputs, FP32 accumulation; §3.1, §4.2: the result is multiplied by the
+// product of the scales; §3.2: global -> shared -> registers -> matrix core ->
+// FP32 accumulators -> epilogue).
+//
+// Matrix core per format:
+//   MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 -- the E8M0 scales ride in the
+//     instruction (one byte per lane per 32-value chunk), so the accumulators
+//     hold the scaled product.  (32x32x64 is the full-rate FP4 form on gfx950;
+//     16x16x128 runs at half rate.)
+//   NVFP4: the instruction scales take only E8M0, so E4M3 16-blocks cannot
+//     ride in it exactly.  E2M1 * E4M3 is exact in FP16, so each wave decodes
+//     its operands to FP16 in registers (v_cvt_scalef32_pk_f16_fp4, then a
+//     packed FP16 multiply by the block scale) and runs
+//     v_mfma_f32_32x32x16_f16; the FP32 tensor scales go to the epilogue.
+//
+// Data path (both formats): one 256 x 256 output tile per workgroup of 8
+// wavefronts (2 per SIMD, 128 x 64 each, 128 accumulators per lane).  K
+// advances in stages of 256 values: the stage's codes (256 rows x 128 B of A
+// and of B) and scale tiles are copied from global memory straight into LDS
+// with buffer_load ... lds, double-buffered.  LDS row r keeps its eight 16-byte
+// chunks c at position c ^ ((r >> 1) & 7), so the operand reads (lane = 32 *
+// chunk parity + row, ds_read_b128) are free of bank conflicts while each
+// load instruction still reads 8 whole 128-byte row segments.  Within a stage,
+// the operands of the next 64-value sub-step are read while the current one
+// multiplies; one barrier per stage.
+//
+// Grouped: the tiles of all experts form one list, ordered expert by expert;
+// every workgroup derives its (expert, m-tile, n-tile) from the device-side
+// group offsets (no host round trip), gathers its A rows through row_idx
+// (codes per lane, scale dwords per lane) and multiplies by that expert's B.
+#include "fp4_launch.h"
+#include "gemm_common.h"
+
+namespace fp4 {
+
+namespace {
+
+constexpr uint32_t BM = 256, BN = 256;
+constexpr uint32_t STAGE_K = 256;                   // K values per stage
+constexpr uint32_t ROW_BYTES = STAGE_K / 2;         // 128 B of codes per row per stage
+constexpr uint32_t REGION = 256 * ROW_BYTES;        // 32 KB of codes per operand per stage
+constexpr uint32_t NSTAGE = 2;
+constexpr uint32_t GROUP_M = 4;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<kFmtMX> {
+  static constexpr uint32_t STILE = 256;  // 32 rows x 8 blocks of 32
+  typedef uint32_t S;                     // per-lane scales of one 32-row block (4 sub-steps)
+};
+template <>
+struct Fmt<kFmtNV> {
+  static constexpr uint32_t STILE = 512;  // 32 rows x 16 blocks of 16
+  typedef u32x2 S;
+};
+
+// Operands of one 64-value K sub-step of a wave's 128 x 64 sub-tile.
+struct Ops {
+  v4i a[4], b[2];
+};
+
+// MXFP4: 8 MFMAs of one sub-step; op_sel SUB picks the sub-step's scale byte.
+template <int SUB>
+__device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const uint32_t (&sa)[4],
+                                        const uint32_t (&sb)[2]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const v8i a8 = __builtin_shufflevector(o.a[r], o.a[r], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const v8i b8 = __builtin_shufflevector(o.b[c], o.b[c], 0, 1, 2, 3, -1, -1, -1, -1);
+      acc[r][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[r][c], 4, 4, SUB, (int)sa[r], SUB,
+                                                                   (int)sb[c]);
+    }
+  }
+}
+
+// NVFP4: the lane's 32 codes of each block split into four groups of 8 (group
+// g lies in the chunk's 16-block g/2), decoded to FP16, one 32x32x16 MFMA per
+// block pair and group.
+template <int SUB>
+__device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u32x2 (&sa)[4],
+                                        const u32x2 (&sb)[2]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int byte = 2 * SUB + (g >> 1);  // scale byte of this group within the lane's 8 bytes
+    v8h a[4], b[2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      a[r] = decode8((uint32_t)o.a[r][g], scale_pair((sa[r][byte >> 2] >> (8 * (byte & 3))) & 0xFFu));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      b[c] = decode8((uint32_t)o.b[c][g], scale_pair((sb[c][byte >> 2] >> (8 * (byte & 3))) & 0xFFu));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[r], b[c], acc[r][c], 0, 0, 0);
+  }
+}
+
+// One LDS read of the next sub-step's operands after each MFMA (MXFP4).
+template <int FMT>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  if (FMT == kFmtMX) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+}
+
+// Grouped problem description (device pointers).
+struct Groups {
+  const int32_t* row_idx;    // output row -> A row
+  const int32_t* group_off;  // E + 1 prefix offsets of the output rows
+  int32_t E;
+  uint32_t A_rows;           // rows of A (tokens)
+  size_t b_codes_stride;     // bytes between experts' codes
+  size_t b_scales_stride;    // bytes between experts' scale buffers
+};
+
+// Locate tile t in the grouped list: tiles of expert e are ceil(cnt_e / BM)
+// m-tiles x tilesN n-tiles, ordered expert by expert.  Returns false past the
+// last tile.  Uniform per workgroup (scalar loads of group_off).
+__device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t t, uint32_t tilesN, uint32_t& e_out,
+                                             uint32_t& row0, uint32_t& rows, uint32_t& tm, uint32_t& tn) {
+  uint32_t first = 0;
+  for (int32_t e = 0; e < gp.E; ++e) {
+    const uint32_t lo = (uint32_t)gp.group_off[e], hi = (uint32_t)gp.group_off[e + 1];
+    const uint32_t cnt = hi - lo;
+    const uint32_t mt = (cnt + BM - 1) / BM;
+    const uint32_t n = mt * tilesN;
+    if (t < first + n) {
+      uint32_t a, b;
+      raster_coords(t - first, mt, tilesN, GROUP_M, a, b);  // grouped raster within the expert
+      e_out = (uint32_t)e;
+      row0 = lo;
+      rows = cnt;
+      tm = a;
+      tn = b;
+      return true;
+    }
+    first += n;
+  }
+  return false;
+}
+
+__device__ __forceinline__ uint32_t grouped_total_tiles(const Groups& gp, uint32_t tilesN) {
+  uint32_t total = 0;
+  for (int32_t e = 0; e < gp.E; ++e) {
+    const uint32_t cnt = (uint32_t)(gp.group_off[e + 1] - gp.group_off[e]);
+    total += ((cnt + BM - 1) / BM) * tilesN;
+  }
+  return total;
+}
+
+template <int FMT, int OUT, bool GROUPED>
+__global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+                                                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB,
+                                                     const float* __restrict__ tsA, const float* __restrict__ tsB,
+                                                     void* __restrict__ C, uint32_t M, uint32_t N, uint32_t K,
+                                                     uint32_t tilesM, uint32_t tilesN, Groups gp) {
+  typedef typename Fmt<FMT>::S S;
+  constexpr uint32_t STILE = Fmt<FMT>::STILE;
+  constexpr uint32_t SCALE_REGION = 8 * STILE;
+  constexpr uint32_t STAGE_BYTES = 2 * REGION + 2 * SCALE_REGION;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE_BYTES];
+
+  const uint32_t ldb = K / 2u;                    // bytes per row of codes
+  const uint32_t KT = (K + 255u) / 256u;          // stages (= scale tiles per row tile)
+  const uint32_t srow = KT * STILE;               // bytes between 32-row scale tiles
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const uint32_t wm = wave >> 2, wn = wave & 3u;  // 2 x 4 waves, 128 x 64 each
+
+  // ---- which tile: rows [row0 + m0, +rowsA) of A / C, columns [n0, +rowsB)
+  uint32_t m0, n0, rowsA, row0 = 0, expert = 0;
+  if (GROUPED) {
+    const uint32_t total = grouped_total_tiles(gp, tilesN);
+    const uint32_t per_xcd = (total + 7u) / 8u;
+    const uint32_t t = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    if ((blockIdx.x >> 3) >= per_xcd || t >= total) return;
+    uint32_t cnt, tm, tn;
+    grouped_tile(gp, t, tilesN, expert, row0, cnt, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    rowsA = (cnt - m0) < BM ? (cnt - m0) : BM;
+    B += (size_t)expert * gp.b_codes_stride;
+    sB += (size_t)expert * gp.b_scales_stride;
+  } else {
+    uint32_t tm, tn;
+    tile_coords(blockIdx.x, tilesM, tilesN, GROUP_M, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    rowsA = (M - m0) < BM ? (M - m0) : BM;
+  }
+  const uint32_t rowsB = (N - n0) < BN ? (N - n0) : BN;
+  const uint8_t* const b_tile = B + (size_t)n0 * ldb;
+  const uint32_t b_bytes = rowsB * ldb;
+  const uint32_t RTB = (N + 31u) / 32u;
+  const uint8_t* const sb_tile = sB + (size_t)(n0 / 32u) * srow;
+  const uint32_t sb_bytes = (RTB > n0 / 32u ? RTB - n0 / 32u : 0u) * srow;
+
+  // ---- direct-to-LDS load plan.  One code load (1 KB) fills 8 rows: lane L
+  // fills LDS row L/8, position L%8, i.e. fetches the row's chunk
+  // (L%8) ^ ((row >> 1) & 7).  Wave w loads row groups w + 8q (q < 4) of A and
+  // of B and scale tile w of A and of B.
+  const uint32_t grow = lane >> 3;
+  const uint32_t gchunk = (lane & 7u) ^ ((4u * (wave & 1u) + (lane >> 4)) & 7u);
+  uint32_t voffA[4], voffB[4];
+  uint32_t svoffA;  // A scale source offset (per lane when grouped)
+  const uint32_t svoffB = (wave * KT) * STILE + lane * 4u;
+  const uint8_t* a_base;
+  uint32_t a_bytes, sa_bytes;
+  const uint8_t* sa_base;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) voffB[q] = (8u * (wave + 8u * q) + grow) * ldb + 16u * gchunk;
+  if (GROUPED) {
+    // Gathered rows: lane offsets from the A row of each tile row; rows past
+    // the group get an out-of-range offset and load zeros.
+    a_base = A;
+    a_bytes = gp.A_rows * ldb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = 8u * (wave + 8u * q) + grow;
+      voffA[q] = r < rowsA ? (uint32_t)gp.row_idx[row0 + m0 + r] * ldb + 16u * gchunk : 0x80000000u;
+    }
+    // Scale dwords: lane L = 32j + i of scale block `wave` is row i, chunk
+    // parity j, found at the gathered row's own scale tile.
+    const uint32_t i = lane & 31u, r = 32u * wave + i;
+    if (r < rowsA) {
+      const uint32_t tok = (uint32_t)gp.row_idx[row0 + m0 + r];
+      svoffA = (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u;
+    } else {
+      svoffA = 0x80000000u;
+    }
+    sa_base = sA;
+    sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
+  } else {
+    a_base = A + (size_t)m0 * ldb;
+    a_bytes = rowsA * ldb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) voffA[q] = voffB[q];
+    const uint32_t RTA = (M + 31u) / 32u;
+    sa_base = sA + (size_t)(m0 / 32u) * srow;
+    sa_bytes = (RTA > m0 / 32u ? RTA - m0 / 32u : 0u) * srow;
+    svoffA = svoffB;
+  }
+
+  auto dma = [&](uint32_t stage_k) {
+    // Stage offsets are folded into the descriptors (scalar registers), so
+    // the per-lane offsets stay loop-invariant.
+    const uint32_t kb = opaque(stage_k * ROW_BYTES);
+    const uint32_t ko = opaque(stage_k * STILE);
+    uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + kb, uniform_rem(a_bytes, kb));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + kb, uniform_rem(b_bytes, kb));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa_base + ko, uniform_rem(sa_bytes, ko));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sb_tile + ko, uniform_rem(sb_bytes, ko));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + 1024u * (wave + 8u * q)), 16, voffA[q], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + REGION + 1024u * (wave + 8u * q)), 16, voffB[q], 0,
+                                               0, 0);
+    }
+#pragma unroll
+    for (uint32_t h = 0; h < STILE / 256u; ++h) {
+      // NVFP4 lanes own 8 bytes: the two halves of a 512-byte tile are lanes
+      // 0-31 and 32-63 of the dword copy.  (Grouped NVFP4 is not offered.)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + 2u * REGION + STILE * wave + 256u * h), 4,
+                                               svoffA + 256u * h, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + 2u * REGION + SCALE_REGION + STILE * wave + 256u * h),
+                                               4, svoffB + 256u * h, 0, 0, 0);
+    }
+  };
+  constexpr int LOADS_PER_STAGE = 8 + 2 * (int)(STILE / 256u);
+
+  // ---- operand reads: lane (j = L/32, i = L%32) of a 32-row block reads row
+  // i, chunk 2q + j of sub-step q, stored at position (2q + j) ^ ((i>>1)&7).
+  const uint32_t li = lane & 31u, lj = lane >> 5;
+  uint32_t rd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rd[q] = 128u * li + 16u * ((2u * q + lj) ^ ((li >> 1) & 7u));
+  const uint32_t a_rows = 128u * (128u * wm);   // byte offset of this wave's first A row
+  const uint32_t b_rows = 128u * (64u * wn);
+
+  auto read_ops = [&](uint32_t stage_k, int q, Ops& o) {
+    const uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.a[r] = *reinterpret_cast<const v4i*>(st + a_rows + 4096u * r + rd[q]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) o.b[c] = *reinterpret_cast<const v4i*>(st + REGION + b_rows + 4096u * c + rd[q]);
+  };
+  auto read_scales = [&](uint32_t stage_k, S (&sa)[4], S (&sb)[2]) {
+    const uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES + 2u * REGION;
+    constexpr uint32_t LB = STILE / 64u;  // bytes per lane
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sa[r] = *reinterpret_cast<const S*>(st + STILE * (4u * wm + r) + LB * lane);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      sb[c] = *reinterpret_cast<const S*>(st + SCALE_REGION + STILE * (2u * wn + c) + LB * lane);
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
+  // Stage k covers K values [256k, 256k + 256) in four 64-value sub-steps.
+  // Sub-steps 0-2 each multiply while the next sub-step's operands are read
+  // from LDS; then wait for this wave's loads of stage k+1, barrier (all of
+  // stage k+1 has landed; every wave is done reading stage k), launch the
+  // loads of stage k+2 into stage k's buffer, read sub-step 0 of k+1 and its
+  // scales, and multiply sub-step 3.  A last, partial stage runs over codes
+  // past K; their scale bytes are the tile's padding (0), which makes those
+  // products zero (E8M0: 2^-127 on both operands, <= 36 * 2^-254, zero in
+  // FP32; E4M3: an FP16 zero), so they add nothing.
+  if (KT > 0) {
+    Ops o0, o1;
+    S sa[4], sb[2], sa_n[4], sb_n[2];
+    dma(0);
+    dma(1);
+    if (LOADS_PER_STAGE == 10)
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_ops(0, 0, o0);
+    read_scales(0, sa, sb);
+    for (uint32_t k = 0; k < KT; ++k) {
+      read_ops(k, 1, o1);
+      mma_sub<0>(acc, o0, sa, sb);
+      interleave_mfma_reads<FMT>();
+      read_ops(k, 2, o0);
+      mma_sub<1>(acc, o1, sa, sb);
+      interleave_mfma_reads<FMT>();
+      read_ops(k, 3, o1);
+      mma_sub<2>(acc, o0, sa, sb);
+      interleave_mfma_reads<FMT>();
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      dma(k + 2u);
+      read_ops(k + 1u, 0, o0);
+      read_scales(k + 1u, sa_n, sb_n);
+      mma_sub<3>(acc, o1, sa, sb);
+      if (FMT == kFmtMX) {
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sa[r] = sa_n[r];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) sb[c] = sb_n[c];
+    }
+  }
+
+  // ---- epilogue: x tsA * tsB, FP32 or BF16 (round to nearest even).  Lane L
+  // of a 32x32 block holds column L%32, rows 8*(i/4) + 4*(L/32) + i%4.
+  const float scale = (tsA ? *tsA : 1.0f) * (tsB ? *tsB : 1.0f);
+  const size_t crow0 = (size_t)row0 + m0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t col = n0 + 64u * wn + 32u * c + li;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t row = 128u * wm + 32u * r + 8u * (i >> 2) + 4u * lj + (i & 3);
+        if (row < rowsA && col < N) {
+          const float v = acc[r][c][i] * scale;
+          if (OUT == 0)
+            static_cast<float*>(C)[(crow0 + row) * N + col] = v;
+          else
+            static_cast<uint16_t*>(C)[(crow0 + row) * N + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, bool GROUPED>
+hipError_t launch(dim3 grid, int out_dtype, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                  const float* tsA, const float* tsB, void* C, uint32_t M, uint32_t N, uint32_t K, uint32_t tilesM,
+                  uint32_t tilesN, const Groups& gp, hipStream_t stream) {
+  if (out_dtype == 0)
+    gemm_kernel<FMT, 0, GROUPED><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
+  else
+    gemm_kernel<FMT, 1, GROUPED><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                             const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, hipStream_t stream) {
+  const uint32_t tilesM = (uint32_t)((M + BM - 1) / BM), tilesN = (uint32_t)((N + BN - 1) / BN);
+  const dim3 grid(tilesM * tilesN);
+  const Groups none{nullptr, nullptr, 0, 0, 0, 0};
+  if (fmt == kFmtNV)
+    return launch<kFmtNV, false>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
+                                 tilesM, tilesN, none, stream);
+  return launch<kFmtMX, false>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
+                               tilesM, tilesN, none, stream);
+}
+
+size_t gemm_grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
+
+bool gemm_grouped_supports(int fmt) { return fmt != kFmtNV; }
+
+hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
+                               const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
+                               const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N,
+                               int64_t K, int fmt, int out_dtype, void* /*workspace*/, hipStream_t stream) {
+  const uint32_t tilesN = (uint32_t)((N + BN - 1) / BN);
+  // Upper bound on the tile count (each expert rounds up at most once), a
+  // multiple of 8 so the XCD-contiguous order covers every tile; workgroups
+  // past the real count return at once.
+  const uint64_t max_tiles = ((uint64_t)(total_rows + BM - 1) / BM + (uint64_t)E) * tilesN;
+  const uint64_t grid = (max_tiles + 7) / 8 * 8;
+  const uint32_t KT = (uint32_t)((K + 255) / 256);
+  const size_t scale_stride = (size_t)((N + 31) / 32) * KT * (fmt == kFmtNV ? 512u : 256u);
+  const Groups gp{row_idx, group_off, E, (uint32_t)A_rows, (size_t)N * (size_t)(K / 2), scale_stride};
+  (void)fmt;
+  return launch<kFmtMX, true>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)total_rows,
+                              (uint32_t)N, (uint32_t)K, 0, tilesN, gp, stream);
+}
+
+}  // namespace fp4

@@ -266,3 +266,94 @@ def test_nvfp4_decode_8192_sampled(orc, M):
     assert to_host(qw.tensor_scale)[0] == np.float32(ts_w)
     Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, cols.size, 8192, 1, tsA=rx[3], tsB=ts_w)
     assert_gemm_close(orc, C[:, cols], Cref, T, True, "decode M=%d" % M)
+
+
+# ---- grouped (mixture-of-experts) GEMM ----------------------------------------
+def _quant_experts(orc, ws, fmt):
+    """Quantise each expert on the GPU into one stacked buffer (codes, scales)
+    and check each against the oracle."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    E = len(ws)
+    N, K = ws[0].shape
+    sbytes = fp4.fp4_scale_bytes(fmt, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    refs = []
+    for e, w in enumerate(ws):
+        q = fp4.Quantized(codes[e], scales[e], None, fmt, N, K)
+        fp4.quantize(to_dev(w), fmt, out=q)
+        r = orc.quantize(w, fmt)
+        np.testing.assert_array_equal(to_host(codes[e]), r[0])
+        np.testing.assert_array_equal(to_host(scales[e]), r[1])
+        refs.append(r)
+    return codes, scales, refs
+
+
+@pytest.mark.parametrize("counts,N,K", [([5, 0, 33, 2], 96, 128), ([300, 1, 0, 257, 17], 160, 544),
+                                        ([0, 0, 0], 64, 64), ([600], 300, 2880), ([1, 1, 1, 1, 1, 1, 1, 1], 520, 256)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_grouped_gemm(orc, counts, N, K, bf16_out):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    fmt = 0
+    counts = np.array(counts)
+    T_rows = max(64, int(counts.max()) if counts.size else 1)
+    row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=int(counts.sum()) + N)
+    x = synth.to_bf16_bits(synth.gaussian(80 + N, (T_rows, K)))
+    ws = [synth.gaussian(90 + e, (N, K), std=0.02) for e in range(counts.size)]
+    say("grouped counts=%s N=%d K=%d" % (counts.tolist(), N, K))
+    qa, ra = _quant_both(orc, x, fmt)
+    codes, scales, _ = _quant_experts(orc, ws, fmt)
+    total = int(off[-1])
+    C = fp4.gemm_grouped(qa, torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda(), codes, scales, N, K,
+                         fmt, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    if total == 0:
+        assert C.numel() == 0
+        return
+    Cg = to_host(C)
+    B = to_host(codes).reshape(-1)
+    sB = to_host(scales).reshape(-1)
+    rows = np.repeat(np.arange(total), N)
+    cols = np.tile(np.arange(N), total)
+    Cref, T = orc.gemm_grouped_sampled(ra[0], ra[1], T_rows, row_idx, off, B, sB, N, K, fmt, rows, cols)
+    assert_gemm_close(orc, Cg.reshape(-1), Cref, T, bf16_out, "grouped")
+
+
+def test_grouped_moe_full_size_sampled(orc):
+    """The MoE workload: 32 experts (5760 x 2880 MXFP4 weights N(0, 0.02^2)),
+    16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4; sampled
+    output rows from every non-empty expert x 24 columns against the oracle."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    E, N, K, T_rows = 32, 5760, 2880, 16384
+    counts = synth.zipf_counts()
+    row_idx, off = synth.moe_routing(counts)
+    x = synth.mxfp4_moe_act()
+    say("grouped moe full size: quantise")
+    qa = fp4.quantize(to_dev(x), 0)
+    sbytes = fp4.fp4_scale_bytes(0, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
+        fp4.quantize(to_dev(w), 0, out=fp4.Quantized(codes[e], scales[e], None, 0, N, K))
+    say("grouped moe full size: gemm")
+    C = fp4.gemm_grouped(qa, torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda(), codes, scales, N, K, 0,
+                         out_dtype=torch.bfloat16)
+    Ch = to_host(C)
+    g = np.random.default_rng(5)
+    cols = np.sort(np.concatenate([[0, N - 1], g.choice(N, 22, replace=False)]))
+    checked = 0
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rs = np.unique(np.concatenate([[lo, hi - 1], g.integers(lo, hi, 2)]))
+        w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
+        rw = orc.quantize(w[cols], 0)
+        rx = orc.quantize(x[row_idx[rs]], 0)
+        Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], rs.size, cols.size, K, 0)
+        assert_gemm_close(orc, Ch[np.ix_(rs, cols)], Cref, T, True, "moe expert %d" % e)
+        checked += rs.size
+    assert checked > 50
