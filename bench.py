@@ -1,17 +1,33 @@
-"""Benchmark of the FP4 block-scaled GEMM path on one MI355X.
+"""Benchmark of the FP4 block-scaled quantise / GEMM path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
 
-Prints ONE JSON line.  The headline workload is the 8192^3 MXFP4 GEMM
-(A, B N(0,1) with 0.2% outliers x20, pre-quantised to 32-blocks with E8M0
-scales, FP32 accumulation, BF16 output): `value` is its throughput in TFLOP/s
-over exactly K timed steps, inputs resident in HBM, with 8 rotating copies of
-the operands so repeated steps cannot be served from the 256 MB Infinity Cache.
-The line also carries the roofline of the dominant kernel (HIP events around
-the timed launches on the launch stream) and the CPU oracle timed on a bounded
-sample of the same workload.
+Prints ONE JSON line.  The headline (`value`) is the 8192^3 MXFP4 GEMM: A and B
+N(0,1) with 0.2% outliers x20, pre-quantised to 32-blocks with E8M0 scales,
+FP32 accumulation, BF16 output; one step = one GEMM; exactly K timed steps
+after W warm-up steps, with 8 rotating copies of the operands so repeated
+steps are not served from the 256 MB Infinity Cache.  The same line carries
+the dominant kernel's roofline (HIP events around the timed launches, on the
+launch stream), the CPU oracle timed on a bounded sample of the same
+workload, and, under "workloads", the other measured workloads:
+
+  nvfp4_decode_m{1,8,32}  W 8192x8192 NVFP4 (pre-quantised), X Mx8192 BF16
+                          quantised on the fly; step = tensor amax + quantise
+                          + decode GEMV; GB/s of algorithmic bytes vs 8 TB/s.
+  nvfp4_mlp               A 4096x4096 BF16 quantised on the fly, W 14336x4096
+                          NVFP4; step = amax + quantise + GEMM; TFLOP/s.
+  mxfp4_moe               32 experts 5760x2880 MXFP4, 16384 BF16 tokens
+                          quantised once per step, Zipf(1.2) top-4 routing;
+                          step = quantise + grouped GEMM; TFLOP/s.
+  mxfp4_256               A, B 256x256 FP32; step = quantise A, B + GEMM (FP32
+                          out); microseconds.
+  mxfp4_quantize_8192     8192x8192 FP32 -> MXFP4; GB/s.
+
+Launch-bound steps (decode, 256^3) are captured once in a HIP graph and
+replayed; every replayed result is checked against the eager one.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,18 +42,254 @@ PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 / FP6 matrix peak
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense FP16 / BF16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 8
+METRIC = "FP4 GEMM TFLOPS & % MXFP4 MFMA peak; decode-shape HBM GB/s & % peak"
 
 
+# ---- algorithmic work -------------------------------------------------------
 def gemm_flops(M, N, K):
     return 2.0 * M * N * K
 
 
-def gemm_bytes(M, N, K, fmt_block=32, out_bytes=2, include_c=True):
-    """Algorithmic bytes of a GEMM on pre-quantised operands: codes (0.5 B per
-    value) and one scale byte per block of each operand read once, C written
-    once."""
-    ab = (M + N) * K * 0.5 + (M + N) * (K // fmt_block)
-    return ab + (M * N * out_bytes if include_c else 0)
+def fp4_operand_bytes(rows, K, block):
+    """Codes (0.5 B per value) plus one scale byte per block."""
+    return rows * K * 0.5 + rows * (K // block)
+
+
+def gemm_bytes(M, N, K, block=32, out_bytes=2, include_c=True):
+    """Algorithmic bytes of a GEMM on pre-quantised operands: each operand's
+    codes and scales read once, C written once."""
+    b = fp4_operand_bytes(M, K, block) + fp4_operand_bytes(N, K, block)
+    return b + (M * N * out_bytes if include_c else 0)
+
+
+def arithmetic_intensity(M, N, K, block=32, out_bytes=2, include_c=True):
+    return gemm_flops(M, N, K) / gemm_bytes(M, N, K, block, out_bytes, include_c)
+
+
+# ---- timing helpers ---------------------------------------------------------
+def time_steps(torch, step, steps, warmup):
+    """Run `warmup` untimed steps, then time exactly `steps` steps with HIP
+    events on the current (launch) stream.  Returns ms per step."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def graph_steps(torch, step, per_graph, check):
+    """Capture `per_graph` steps (rotating inputs) into one HIP graph; returns
+    a replay function.  `check()` compares the step's output with an eager
+    result after each of a few replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            step(i)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        check()
+    return g
+
+
+def to_dev(torch, x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(kernel_src):
+    """HBM traffic of the headline kernel from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_mxfp4_8192_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha256_16") != src_hash(kernel_src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ---- workloads --------------------------------------------------------------
+def mxfp4_gemm_8192(torch, fp4, synth, args):
+    n = 8192
+    a, b = synth.mxfp4_8192(n)
+    qa0 = fp4.quantize(to_dev(torch, a), fp4.MXFP4)
+    qb0 = fp4.quantize(to_dev(torch, b), fp4.MXFP4)
+    qa = [qa0] + [fp4.Quantized(qa0.codes.clone(), qa0.scales.clone(), None, fp4.MXFP4, n, n)
+                  for _ in range(ROTATE - 1)]
+    qb = [qb0] + [fp4.Quantized(qb0.codes.clone(), qb0.scales.clone(), None, fp4.MXFP4, n, n)
+                  for _ in range(ROTATE - 1)]
+    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        fp4.gemm(qa[i % ROTATE], qb[i % ROTATE], out=C)
+
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    tflops = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
+    return dict(ms=ms, tflops=tflops, a=a, b=b)
+
+
+def cpu_baseline_gemm(a, b, K, budget_s=12.0):
+    """The oracle (quantise + FP64 GEMM) on a slab of the 8192^3 workload,
+    sized to roughly `budget_s` seconds; TFLOP/s of the slab's arithmetic."""
+    import oracle
+    t0 = time.perf_counter()
+    ra = oracle.quantize(a[:64], oracle.FMT_MXFP4)
+    rb = oracle.quantize(b[:64], oracle.FMT_MXFP4)
+    oracle.gemm(ra[0], ra[1], rb[0], rb[1], 64, 64, K, oracle.FMT_MXFP4)
+    dt = time.perf_counter() - t0
+    cols = int(max(64, min(8192, 64 * budget_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    ra = oracle.quantize(a[:64], oracle.FMT_MXFP4)
+    rb = oracle.quantize(b[:cols], oracle.FMT_MXFP4)
+    oracle.gemm(ra[0], ra[1], rb[0], rb[1], 64, cols, K, oracle.FMT_MXFP4)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(gemm_flops(64, cols, K) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "oracle MXFP4 quantise of 64 rows of A and %d rows of B plus FP64 GEMM 64x%dx%d of the "
+                      "8192^3 workload, %.1f s" % (cols, cols, K, dt)}
+
+
+def nvfp4_decode(torch, fp4, synth, M):
+    N = K = 8192
+    w = synth.nvfp4_decode_weight()
+    qw0 = fp4.quantize(to_dev(torch, w), fp4.NVFP4)
+    del w
+    qw = [qw0] + [fp4.Quantized(qw0.codes.clone(), qw0.scales.clone(), qw0.tensor_scale.clone(), fp4.NVFP4, N, K)
+                  for _ in range(ROTATE - 1)]
+    x = to_dev(torch, synth.nvfp4_decode_act(M))
+    qx = fp4.quantize(x, fp4.NVFP4)  # output buffers reused by every step
+    wsq = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, M, 0, K)
+    wsg = fp4.workspace(fp4.OP_GEMM, fp4.NVFP4, M, N, K)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp4.quantize(x, fp4.NVFP4, ws=wsq, out=qx)
+        fp4.gemm(qx, qw[i % ROTATE], out=C, ws=wsg)
+
+    step(0)
+    torch.cuda.synchronize()
+    ref = C.clone()
+
+    def check():
+        assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), "graph replay differs from eager"
+
+    per_graph = ROTATE * 4
+    g = graph_steps(torch, step, per_graph, check)
+    reps = 30
+    ms = time_steps(torch, lambda i: g.replay(), reps, 3) / per_graph
+    nbytes = fp4_operand_bytes(N, K, 16) + M * K * 2 + M * N * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"M": M, "N": N, "K": K, "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": int(nbytes),
+            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "step": "tensor amax + NVFP4 quantise of X + decode GEMV (HIP graph replay)"}
+
+
+def nvfp4_mlp(torch, fp4, synth):
+    M, N, K = 4096, 14336, 4096
+    a, w = synth.nvfp4_mlp()
+    x = to_dev(torch, a)
+    qw = fp4.quantize(to_dev(torch, w), fp4.NVFP4)
+    del a, w
+    qx = fp4.quantize(x, fp4.NVFP4)
+    wsq = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, M, 0, K)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp4.quantize(x, fp4.NVFP4, ws=wsq, out=qx)
+        fp4.gemm(qx, qw, out=C)
+
+    ms = time_steps(torch, step, 20, 3)
+    tf = gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+    return {"M": M, "N": N, "K": K, "ms_per_step": round(ms, 4), "TFLOP_per_s": round(tf, 1),
+            "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4), "frac_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4),
+            "step": "tensor amax + NVFP4 quantise of A (BF16) + NVFP4 GEMM (FP16 matrix core), BF16 out"}
+
+
+def mxfp4_moe(torch, fp4, synth):
+    E, N, K, T = 32, 5760, 2880, 16384
+    counts = synth.zipf_counts()
+    row_idx, off = synth.moe_routing(counts)
+    x = to_dev(torch, synth.mxfp4_moe_act())
+    sbytes = fp4.fp4_scale_bytes(fp4.MXFP4, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
+        fp4.quantize(to_dev(torch, w), fp4.MXFP4, out=fp4.Quantized(codes[e], scales[e], None, fp4.MXFP4, N, K))
+    qx = fp4.quantize(x, fp4.MXFP4)
+    ri = torch.from_numpy(row_idx).cuda()
+    go = torch.from_numpy(off).cuda()
+    total = int(off[-1])
+    C = torch.empty((total, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp4.quantize(x, fp4.MXFP4, out=qx)
+        fp4.gemm_grouped(qx, ri, go, codes, scales, N, K, fp4.MXFP4, out=C)
+
+    ms = time_steps(torch, step, 10, 2)
+    tf = gemm_flops(total, N, K) / (ms * 1e-3) / 1e12
+    nonempty = int((counts > 0).sum())
+    nbytes = (nonempty * fp4_operand_bytes(N, K, 32) + T * K * 2 + fp4_operand_bytes(T, K, 32) * 2 + total * N * 2)
+    return {"experts": E, "N": N, "K": K, "tokens": T, "routed_rows": total, "ms_per_step": round(ms, 4),
+            "TFLOP_per_s": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+            "algorithmic_bytes": int(nbytes),
+            "step": "MXFP4 quantise of the 16384 tokens (BF16) + grouped GEMM, BF16 out"}
+
+
+def mxfp4_256(torch, fp4, synth):
+    a, b = synth.mxfp4_256()
+    xa, xb = to_dev(torch, a), to_dev(torch, b)
+    qa = fp4.quantize(xa, fp4.MXFP4)
+    qb = fp4.quantize(xb, fp4.MXFP4)
+    C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        fp4.quantize(xa, fp4.MXFP4, out=qa)
+        fp4.quantize(xb, fp4.MXFP4, out=qb)
+        fp4.gemm(qa, qb, out=C)
+
+    step(0)
+    torch.cuda.synchronize()
+    ref = C.clone()
+
+    def check():
+        assert torch.equal(C, ref), "graph replay differs from eager"
+
+    g = graph_steps(torch, step, 32, check)
+    ms = time_steps(torch, lambda i: g.replay(), 30, 3) / 32
+    return {"us_per_step": round(ms * 1e3, 3), "TFLOP_per_s": round(gemm_flops(256, 256, 256) / (ms * 1e-3) / 1e12, 3),
+            "step": "MXFP4 quantise of A and B (FP32) + GEMM, FP32 out (HIP graph replay)"}
+
+
+def mxfp4_quantize_8192(torch, fp4, a):
+    x = to_dev(torch, a)
+    q = fp4.quantize(x, fp4.MXFP4)
+    ms = time_steps(torch, lambda i: fp4.quantize(x, fp4.MXFP4, out=q), 50, 5)
+    n = a.size
+    nbytes = n * 4 + fp4_operand_bytes(a.shape[0], a.shape[1], 32)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us_per_step": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def parse():
@@ -45,93 +297,79 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mxfp4_8192")
+    p.add_argument("--only", default=None, help="run only the headline (mxfp4_gemm_8192) or one other workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 256 MiB device copy (x*1 -> y) 3 times, to scale the HBM byte counters")
     return p.parse_args()
 
 
-def cpu_baseline_gemm(a, b, K, budget_s=12.0):
-    """The oracle (quantise + FP64 GEMM) on a slab of the 8192^3 workload: a
-    few rows of A against a few rows of B, sized to roughly `budget_s` seconds;
-    reported in TFLOP/s of the full problem's arithmetic."""
-    import oracle
-    rows = 8
-    t0 = time.perf_counter()
-    ra = oracle.quantize(a[:rows], oracle.FMT_MXFP4)
-    rb = oracle.quantize(b[:rows], oracle.FMT_MXFP4)
-    oracle.gemm(ra[0], ra[1], rb[0], rb[1], rows, rows, K, oracle.FMT_MXFP4)
-    dt = time.perf_counter() - t0
-    cols = int(max(8, min(4096, rows * budget_s / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    ra = oracle.quantize(a[:64], oracle.FMT_MXFP4)
-    rb = oracle.quantize(b[:cols], oracle.FMT_MXFP4)
-    oracle.gemm(ra[0], ra[1], rb[0], rb[1], 64, cols, K, oracle.FMT_MXFP4)
-    dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": gemm_flops(64, cols, K) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "oracle MXFP4 quantise of 64 rows of A and %d rows of B plus FP64 GEMM 64x%dx%d "
-                      "(%.1f s)" % (cols, cols, K, dt)}
-
-
-def bench_mxfp4_8192(args, torch, fp4):
-    import synth
-    n = 8192
-    a, b = synth.mxfp4_8192(n)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_gemm(a, b, n)
-    qa = [fp4.quantize(torch.from_numpy(a).cuda(), fp4.MXFP4)]
-    qb = [fp4.quantize(torch.from_numpy(b).cuda(), fp4.MXFP4)]
-    del a, b
-    for _ in range(ROTATE - 1):
-        qa.append(fp4.Quantized(qa[0].codes.clone(), qa[0].scales.clone(), None, fp4.MXFP4, n, n))
-        qb.append(fp4.Quantized(qb[0].codes.clone(), qb[0].scales.clone(), None, fp4.MXFP4, n, n))
-    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+def calibrate_copy(torch):
+    n = 64 << 20
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.mul(x, 1.0, out=y)
     torch.cuda.synchronize()
-
-    def step(i):
-        fp4.gemm(qa[i % ROTATE], qb[i % ROTATE], out=C)
-
-    return step, cpu, dict(M=n, N=n, K=n)
+    print(json.dumps({"copy_kernel": "torch.mul(x, 1.0, out=y)", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 3}))
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+        print("bench.py measures one GPU: this library runs on a single MI355X and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
+
     import block_scaled_fp4_03_amd as fp4
+    import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.workload != "mxfp4_8192":
-        raise SystemExit("unknown workload " + args.workload)
-    step, cpu, shp = bench_mxfp4_8192(args, torch, fp4)
-    M, N, K = shp["M"], shp["N"], shp["K"]
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    flops = gemm_flops(M, N, K)
-    tflops = flops / (ms * 1e-3) / 1e12
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    t_start = time.perf_counter()
+
+    head = mxfp4_gemm_8192(torch, fp4, synth, args)
+    sys.stderr.write("[bench] mxfp4_gemm_8192 %.4f ms %.1f TFLOP/s\n" % (head["ms"], head["tflops"]))
+    cpu = None if args.no_cpu_baseline else cpu_baseline_gemm(head["a"], head["b"], 8192)
+    sys.stderr.write("[bench] cpu_baseline %s\n" % json.dumps(cpu))
+
+    extra = {}
+    a8192 = head.pop("a")
+    del head["b"]
+    todo = [("mxfp4_quantize_8192", lambda: mxfp4_quantize_8192(torch, fp4, a8192)),
+            ("nvfp4_decode_m1", lambda: nvfp4_decode(torch, fp4, synth, 1)),
+            ("nvfp4_decode_m8", lambda: nvfp4_decode(torch, fp4, synth, 8)),
+            ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),
+            ("nvfp4_mlp", lambda: nvfp4_mlp(torch, fp4, synth)),
+            ("mxfp4_moe", lambda: mxfp4_moe(torch, fp4, synth)),
+            ("mxfp4_256", lambda: mxfp4_256(torch, fp4, synth))]
+    for name, fn in todo:
+        if args.only is not None and args.only != name:
+            continue
+        extra[name] = fn()
+        torch.cuda.empty_cache()
+        sys.stderr.write("[bench] %s %s\n" % (name, json.dumps(extra[name])))
+
+    kernel_src = os.path.join(ROOT, "block_scaled_fp4_03_amd", "csrc", "gemm.hip")
+    tflops = head["tflops"]
     line = {
-        "metric": "FP4 GEMM TFLOPS & % MXFP4 MFMA peak; decode-shape HBM GB/s & % peak",
+        "metric": METRIC,
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(head["ms"], 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4", "data": "synthetic",
-        "config": {"workload": "mxfp4_gemm_8192x8192x8192", "M": M, "N": N, "K": K, "out": "bf16",
-                   "parallelism": "single-gpu"},
+        "config": {"workload": "mxfp4_gemm_8192x8192x8192", "M": 8192, "N": 8192, "K": 8192,
+                   "operands": "pre-quantised MXFP4 (E2M1 codes, E8M0 32-blocks), N(0,1) with 0.2% outliers x20",
+                   "out": "bf16", "accumulate": "fp32", "parallelism": "single-gpu", "rotating_copies": ROTATE},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_FP4_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_mx_kernel"},
+                     "frac": round(tflops / PEAK_FP4_TFLOPS, 4), "traffic": traffic_record(kernel_src),
+                     "kernel": "gemm_kernel<MXFP4, BF16, dense>",
+                     "algorithmic_flops_per_launch": gemm_flops(8192, 8192, 8192)},
         "cpu_baseline": cpu,
-        "wall_s": round(wall, 3),
+        "workloads": extra,
+        "wall_s": round(time.perf_counter() - t_start, 1),
     }
     print(json.dumps(line))
 

@@ -40,7 +40,7 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
     case FP4_OP_QUANTIZE:
       return fmt == FP4_NVFP4 ? 8 : 0;
     case FP4_OP_GEMM:
-      return (fmt == FP4_NVFP4 && fp4::gemv_nv_applies(M, N)) ? fp4::gemv_nv_workspace(M, N, K) : 0;
+      return 0;
     case FP4_OP_GEMM_GROUPED:
       return fp4::gemm_grouped_workspace(M, N, K, E);
     default:
@@ -105,11 +105,8 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
   if (!aligned(tsA, 4) || !aligned(tsB, 4)) return FP4_ERR_ALIGN;
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
-  if (nv && fp4::gemv_nv_applies(M, N)) {
-    const size_t need = fp4::gemv_nv_workspace(M, N, K);
-    if (!workspace || workspace_bytes < need) return FP4_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return FP4_ERR_ALIGN;
-    return launched(fp4::launch_gemv_nv(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, workspace, s));
+  if (nv && fp4::gemv_nv_applies(M, N, K)) {
+    return launched(fp4::launch_gemv_nv(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
   }
   return launched(fp4::launch_gemm_tiled(fmt, A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
 }

@@ -116,6 +116,17 @@ __device__ __forceinline__ v2h scale_pair(uint32_t b) {
   return __builtin_bit_cast(v2h, h | (h << 16));
 }
 
+// Two E4M3 bytes (bits 0-15 of w, or 16-31 when HI) as two FP16 values: the
+// gfx950 FP8 converter with a unit scale is exact for every finite byte,
+// subnormals included.
+template <bool HI>
+__device__ __forceinline__ v2h e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+__device__ __forceinline__ v2h splat_lo(v2h p) { return __builtin_shufflevector(p, p, 0, 0); }
+__device__ __forceinline__ v2h splat_hi(v2h p) { return __builtin_shufflevector(p, p, 1, 1); }
+
 // Eight FP16 values = E2M1 codes of one dword (low nibble first) times s.
 // The gfx950 converter gives each code's E2M1 value (scale operand 1.0); the
 // packed multiply by the E4M3 scale is exact.

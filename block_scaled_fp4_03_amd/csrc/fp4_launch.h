@@ -31,10 +31,9 @@ hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_ro
                                int64_t K, int fmt, int out_dtype, void* workspace, hipStream_t stream);
 
 // NVFP4 decode GEMV / skinny GEMM for M <= 32 (gemv_nv.hip).
-bool gemv_nv_applies(int64_t M, int64_t N);
-size_t gemv_nv_workspace(int64_t M, int64_t N, int64_t K);
+bool gemv_nv_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
-                          int out_dtype, void* workspace, hipStream_t stream);
+                          int out_dtype, hipStream_t stream);
 
 }  // namespace fp4

@@ -18,200 +18,280 @@ namespace {
 // weights ("Rubin FP4 GEMM deep dive" §1.2, §6.2: decoding streams every
 // weight once, so it is bound by memory bandwidth).
 //
-// Workgroup = 4 wavefronts = 128 weight rows x one K slice of SPLIT 256-value
-// tiles.  Each wave owns 32 weight rows and issues all of its slice's code and
-// scale loads at once (32 KB per wave in flight), then, while they land, the
-// workgroup decodes its activation slice once into LDS as FP16 in the
-// matrix-core operand order (rows >= M are zero).  Per 64-value sub-step a
-// lane holds 32 weight codes (chunk 2s + j of its row, the scale layout's lane
-// order) and runs four 32x32x16 FP16 MFMAs against the activation operands
-// read from LDS.  Partial sums of the K slices go to the workspace; the last
-// workgroup of a column block (atomic counter, reset afterwards) adds them in
-// slice order, applies tsA * tsB and writes C.
+// Workgroup = 16 wavefronts (4 per SIMD, so loads of some waves overlap the
+// decode and MFMAs of others) = one 32-row block of W over the whole of K,
+// more blocks in a grid-stride loop when N is large.  Wave w takes the
+// 256-value tiles kt = w, w + 16, ...; per tile a lane loads 32 bytes of its
+// W row (chunk 2s + j of the row, the scale layout's lane order) and the 8
+// scale bytes of its lane.  A wave asks for its next tile only once the
+// current one is decoded (ring depth GV_PD = 1): the chip then receives the
+// weights in K order, tile column by tile column, and decodes one column while
+// the next is in flight; requesting everything at once (depth 2) makes every
+// tile land near the end of the transfer and measured 20% slower.
+//
+// The activation is staged once per workgroup in LDS, in one of two forms:
+//   AF16  (small M x K): the exact FP16 values, row-major, rows padded by 16 B
+//         so the MFMA operand reads are free of bank conflicts; rows >= M
+//         read a zeroed 512-byte block.  No decode work per MFMA.
+//   ACODE (otherwise): the packed codes in MFMA operand order
+//         ([tile][sub-step][lane] x 16 B) and the scale tiles verbatim; each
+//         MFMA decodes its A operand.  Rows >= M are zero codes.
+// At the end of a row block the 16 waves' partial sums are added in a fixed
+// order through LDS (deterministic); no exchange between workgroups and no
+// workspace.
 // ---------------------------------------------------------------------------
-constexpr uint32_t GV_ROWS = 128;       // weight rows per workgroup
-constexpr uint32_t GV_MAX_SPLIT = 8;    // 256-value tiles per K slice
+constexpr uint32_t GV_WAVES = 16;               // wavefronts per workgroup (K split)
+constexpr uint32_t GV_PD = 1;                   // weight tiles in flight per wave
+constexpr uint32_t GV_RED_BYTES = 4u * 32u * 32u * 4u;         // 4 partial-sum slots
+constexpr uint32_t GV_A_BYTES = 160u * 1024u - GV_RED_BYTES;    // activation staging
+// 16-byte activation loads per thread (at most): FP16 staging, code staging.
+constexpr uint32_t GV_A_LOADS_F16 = 3;
+constexpr uint32_t GV_A_LOADS_CODE = 8;
 
-template <int OUT, int SPLIT>
-__global__ __launch_bounds__(256) void gemv_nv_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
-                                                        const uint8_t* __restrict__ W, const uint8_t* __restrict__ sW,
-                                                        const float* __restrict__ tsA, const float* __restrict__ tsW,
-                                                        void* __restrict__ C, float* __restrict__ partial,
-                                                        uint32_t* __restrict__ counters, uint32_t M, uint32_t N,
-                                                        uint32_t K, uint32_t KS) {
-  // A operands: [tile][sub-step s][group t][lane] x 16 B (8 FP16).
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[SPLIT * 16 * 1024];
-  __shared__ uint32_t last_flag;
+enum { kAF16 = 0, kACode = 1 };
 
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t nb = blockIdx.x / KS, ks = blockIdx.x % KS;
-  const uint32_t n0 = nb * GV_ROWS + 32u * wave;       // this wave's first weight row
-  const uint32_t KT = (K + 255u) / 256u;
-  const uint32_t kt0 = ks * SPLIT;                     // first 256-value tile of the slice
-  const uint32_t ldb = K / 2u;
+struct GvTile {
+  v4i w[4];   // codes: 32 values per lane per 64-value sub-step
+  u32x2 ws;   // the lane's 8 scale bytes (4 sub-steps x 2 blocks)
+};
+
+template <int AMODE, int OUT>
+__global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ W,
+    const uint8_t* __restrict__ sW, const float* __restrict__ tsA, const float* __restrict__ tsW, void* __restrict__ C,
+    uint32_t M, uint32_t N, uint32_t K) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[GV_A_BYTES];
+  __shared__ float red[4][32][32];
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t li = lane & 31u, lj = lane >> 5;
+  const uint32_t KT = (K + 255u) / 256u;
+  const uint32_t Kp = KT * 256u;
+  // Tiles per wave per row block (at least one, so that K == 0 still stores zeros).
+  const uint32_t NJ = KT > GV_WAVES ? (KT + GV_WAVES - 1u) / GV_WAVES : 1u;
+  const uint32_t ldb = K / 2u;
+  const uint32_t srow = KT * 512u;                         // scale bytes per 32-row tile row
+  const uint32_t nblocks = (N + 31u) / 32u;
+  const uint32_t nrb = (nblocks - blockIdx.x + gridDim.x - 1u) / gridDim.x;  // row blocks of this workgroup
+  const uint32_t T = NJ * nrb;                              // work items of this wave
+  const uint32_t RS = 2u * Kp + 16u;                        // AF16 row stride (bytes)
+  const uint32_t zero_off = M * RS;                         // AF16: 512 zero bytes
 
-  // ---- issue every weight load of the slice (codes 16 B per sub-step, scale
-  // 8 B per tile); rows past N and tiles past K read as zero.
-  const uint32_t wrows = N > n0 ? (N - n0 < 32u ? N - n0 : 32u) : 0u;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * ldb, wrows * ldb);
-  const uint32_t srow = KT * 512u;
-  const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(sW + (size_t)(n0 / 32u) * srow, (n0 < N) ? srow : 0u);
-  v4i wc[SPLIT][4];
-  u32x2 wsc[SPLIT];
+  // ---- activation loads (issued before the weights: waits are in order)
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, M * ldb);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sA, srow);
+  constexpr int NA = AMODE == kAF16 ? (int)GV_A_LOADS_F16 : (int)GV_A_LOADS_CODE;
+  v4i ald[NA];
+  uint32_t asc[NA];
 #pragma unroll
-  for (int t = 0; t < SPLIT; ++t) {
-    const uint32_t kt = kt0 + t;
-    const uint32_t ok = kt < KT;
+  for (int i = 0; i < NA; ++i) {
+    const uint32_t c = tid + 1024u * i;   // 16-byte chunk handled by this thread
+    uint32_t off = 0x80000000u, soff = 0x80000000u;
+    if (AMODE == kAF16) {
+      const uint32_t cpr = Kp / 32u;       // chunks per row
+      const uint32_t row = c / cpr, cc = c % cpr;
+      if (row < M && cc * 16u < ldb) {
+        off = row * ldb + cc * 16u;
+        soff = scale_offset<kFmtNV>(row, 2u * cc, KT);
+      }
+      asc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
+    } else {
+      if (c < KT * 256u) {                  // operand-order chunk: tile, sub-step, lane
+        const uint32_t blk = c >> 6, L = c & 63u;
+        const uint32_t row = L & 31u;
+        if (row < M) off = row * ldb + (blk >> 2) * 128u + (blk & 3u) * 32u + 16u * (L >> 5);
+      }
+    }
+    ald[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+  }
+  v4i ascl = v4i{};
+  if (AMODE == kACode) {
+    // scale tiles verbatim: KT x 512 B = KT * 32 chunks (<= 1 per thread for KT <= 32)
+    const uint32_t c = tid;
+    ascl = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsa, c < KT * 32u ? c * 16u : 0x80000000u, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- weight ring prologue
+  const uint32_t lane_off = li * ldb + 16u * lj;
+  GvTile ring[GV_PD];
+  auto issue = [&](GvTile& d, uint32_t j) {
+    const uint32_t rb = blockIdx.x + (j / NJ) * gridDim.x;
+    const uint32_t kt = wave + GV_WAVES * (j % NJ);
+    const uint32_t n0 = rb * 32u;
+    const uint32_t rows = __builtin_amdgcn_readfirstlane(N - n0 < 32u ? N - n0 : 32u);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * ldb, rows * ldb);
+    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sW + (size_t)rb * srow, srow);
+    const bool ok = kt < KT;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t off = ok ? li * ldb + kt * 128u + 32u * s2 + 16u * lj : 0x80000000u;
-      wc[t][s2] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+      const uint32_t off = ok ? lane_off + kt * 128u + 32u * s2 : 0x80000000u;
+      d.w[s2] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
     }
-    const uint32_t soff = ok ? kt * 512u + 8u * lane : 0x80000000u;
-    wsc[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsw, soff, 0, 0));
-  }
+    d.ws = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsw, ok ? kt * 512u + 8u * lane : 0x80000000u,
+                                                                          0, 0));
+  };
+#pragma unroll
+  for (int p = 0; p < (int)GV_PD; ++p)
+    if ((uint32_t)p < T) issue(ring[p], p);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- activation slice -> LDS (FP16, operand order).  Thread = (row, chunk)
-  // of each tile: row i = tid % 32, chunk c = tid / 32 (0..7).
-  {
-    const uint32_t tid = threadIdx.x;
-    const uint32_t i = tid & 31u, c = tid >> 5;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, M * ldb);
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sA, KT * 512u);
+  // ---- activation -> LDS
 #pragma unroll
-    for (int t = 0; t < SPLIT; ++t) {
-      const uint32_t kt = kt0 + t;
-      const bool ok = kt < KT && i < M;
-      const uint32_t off = ok ? i * ldb + kt * 128u + 16u * c : 0x80000000u;
-      const v4i codes = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-      const uint32_t slane = 32u * (c & 1u) + i, s = c >> 1;
-      const uint32_t soff = ok ? kt * 512u + 8u * slane + 2u * s : 0x80000000u;
-      const uint32_t sc2 = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
-      const v2h s0 = scale_pair(sc2 & 0xFFu), s1 = scale_pair(sc2 >> 8);
-      uint8_t* dst = lds_a + ((t * 4u + s) * 4u) * 1024u + (32u * (c & 1u) + i) * 16u;
+  for (int i = 0; i < NA; ++i) {
+    const uint32_t c = tid + 1024u * i;
+    if (AMODE == kAF16) {
+      const uint32_t cpr = Kp / 32u;
+      const uint32_t row = c / cpr, cc = c % cpr;
+      if (row < M) {
+        const v2h s0 = scale_pair(asc[i] & 0xFFu), s1 = scale_pair((asc[i] >> 8) & 0xFFu);
+        uint8_t* dst = lds_a + row * RS + cc * 64u;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<v8h*>(dst + g * 1024u) = decode8((uint32_t)codes[g], g < 2 ? s0 : s1);
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<v8h*>(dst + 16u * g) = decode8((uint32_t)ald[i][g], g < 2 ? s0 : s1);
+      }
+    } else {
+      if (c < KT * 256u) *reinterpret_cast<v4i*>(lds_a + 16u * c) = ald[i];
     }
   }
+  if (AMODE == kACode && tid < KT * 32u) *reinterpret_cast<v4i*>(lds_a + KT * 4096u + 16u * tid) = ascl;
+  if (AMODE == kAF16 && tid < 32u) *reinterpret_cast<v4i*>(lds_a + zero_off + 16u * tid) = v4i{};
   __syncthreads();
 
-  // ---- weights x activation
-  v16f acc = v16f{};
+  // ---- main loop
+  const float scale = *tsA * *tsW;
+  // AF16: lanes of rows >= M read a 512-byte zero block at a fixed place.
+  const uint32_t a_row_off = li * RS + 64u * lj;
+  v16f acc0 = v16f{}, acc1 = v16f{};
+  for (uint32_t jj = 0; jj < T; jj += GV_PD) {
 #pragma unroll
-  for (int t = 0; t < SPLIT; ++t) {
+    for (int p = 0; p < (int)GV_PD; ++p) {
+      const uint32_t j = jj + p;
+      if (j >= T) break;
+      const uint32_t kt = wave + GV_WAVES * (j % NJ);
+      if (kt < KT) {
+        const GvTile& d = ring[p];
+        const uint32_t abase = li < M ? a_row_off + kt * 512u : zero_off;
+        u32x2 as2 = u32x2{};
+        if (AMODE == kACode) as2 = *reinterpret_cast<const u32x2*>(lds_a + KT * 4096u + kt * 512u + 8u * lane);
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t sw = wsc[t][s2 >> 1] >> (16 * (s2 & 1));
-      const v2h w0 = scale_pair(sw & 0xFFu), w1 = scale_pair((sw >> 8) & 0xFFu);
+        for (int s2 = 0; s2 < 4; ++s2) {
+          // scale bytes 2*s2 (blocks of words 0, 1) and 2*s2 + 1 (words 2, 3)
+          const v2h wsp = (s2 & 1) ? e4m3x2_to_f16<true>(d.ws[s2 >> 1]) : e4m3x2_to_f16<false>(d.ws[s2 >> 1]);
+          const v2h w0 = splat_lo(wsp), w1 = splat_hi(wsp);
+          v4i acodes = v4i{};
+          v2h a0 = v2h{}, a1 = v2h{};
+          if (AMODE == kACode) {
+            acodes = *reinterpret_cast<const v4i*>(lds_a + (kt * 4u + s2) * 1024u + 16u * lane);
+            const v2h asp = (s2 & 1) ? e4m3x2_to_f16<true>(as2[s2 >> 1]) : e4m3x2_to_f16<false>(as2[s2 >> 1]);
+            a0 = splat_lo(asp);
+            a1 = splat_hi(asp);
+          }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const v8h b = decode8((uint32_t)wc[t][s2][g], g < 2 ? w0 : w1);
-        const v8h a = *reinterpret_cast<const v8h*>(lds_a + ((t * 4u + s2) * 4u + g) * 1024u + lane * 16u);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+          for (int g = 0; g < 4; ++g) {
+            const v8h b = decode8((uint32_t)d.w[s2][g], g < 2 ? w0 : w1);
+            v8h a;
+            if (AMODE == kAF16)
+              a = *reinterpret_cast<const v8h*>(lds_a + abase + s2 * 128u + 16u * g);
+            else
+              a = decode8((uint32_t)acodes[g], g < 2 ? a0 : a1);
+            if (g & 1)
+              acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc1, 0, 0, 0);
+            else
+              acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc0, 0, 0, 0);
+          }
+        }
+      }
+      if (j + GV_PD < T) issue(ring[p], j + GV_PD);
+
+      if (j % NJ == NJ - 1u) {
+        // End of a row block: waves 0..3 gather waves 4..15 (in order of w),
+        // then wave 0 gathers 1..3, scales and stores.  Lane L holds column
+        // n0 + L%32 and rows 8(i/4) + 4(L/32) + i%4.
+        const uint32_t n0 = (blockIdx.x + (j / NJ) * gridDim.x) * 32u;
+        v16f acc = acc0 + acc1;
+#pragma unroll
+        for (uint32_t r = 1; r < GV_WAVES / 4u; ++r) {
+          if (wave / 4u == r) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+              if (m < M) red[wave & 3u][m][li] = acc[i];
+            }
+          }
+          __syncthreads();
+          if (wave < 4u) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+              if (m < M) acc[i] += red[wave][m][li];
+            }
+          }
+          __syncthreads();
+        }
+        if (wave >= 1u && wave < 4u) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+            if (m < M) red[wave][m][li] = acc[i];
+          }
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const uint32_t col = n0 + li;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+            if (m < M && col < N) {
+              const float v = (((acc[i] + red[1][m][li]) + red[2][m][li]) + red[3][m][li]) * scale;
+              if (OUT == 0)
+                static_cast<float*>(C)[(size_t)m * N + col] = v;
+              else
+                static_cast<uint16_t*>(C)[(size_t)m * N + col] = f32_to_bf16(v);
+            }
+          }
+        }
+        __syncthreads();
+        acc0 = v16f{};
+        acc1 = v16f{};
       }
     }
   }
-
-  // ---- partials: lane L holds column n0 + L%32 and rows 8(i/4) + 4(L/32) + i%4
-  const uint32_t col = n0 + li;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
-    if (m < M && col < N) partial[((size_t)ks * M + m) * N + col] = acc[i];
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = atomicAdd(&counters[nb], 1u);
-    last_flag = (done == KS - 1u);
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const float scale = *tsA * *tsW;
-  const uint32_t cbase = nb * GV_ROWS;
-  for (uint32_t e = threadIdx.x; e < M * GV_ROWS; e += 256u) {
-    const uint32_t m = e / GV_ROWS, n = cbase + e % GV_ROWS;
-    if (n >= N) continue;
-    float sum = 0.0f;
-    for (uint32_t q = 0; q < KS; ++q) sum += partial[((size_t)q * M + m) * N + n];
-    const float v = sum * scale;
-    if (OUT == 0)
-      static_cast<float*>(C)[(size_t)m * N + n] = v;
-    else
-      static_cast<uint16_t*>(C)[(size_t)m * N + n] = f32_to_bf16(v);
-  }
-  if (threadIdx.x == 0) counters[nb] = 0u;
 }
 
-// Split of K for the decode path: at least ~256 workgroups, at most
-// GV_MAX_SPLIT tiles per slice.
-struct GemvPlan {
-  uint32_t nblocks, split, ks;
-};
-
-static GemvPlan gemv_plan(int64_t N, int64_t K) {
-  GemvPlan p;
-  p.nblocks = (uint32_t)((N + GV_ROWS - 1) / GV_ROWS);
-  const uint32_t KT = (uint32_t)((K + 255) / 256);
-  uint32_t want = (256u + p.nblocks - 1u) / p.nblocks;      // slices wanted for ~256 WGs
-  if (want < 1u) want = 1u;
-  uint32_t split = (KT + want - 1u) / want;
-  if (split > GV_MAX_SPLIT) split = GV_MAX_SPLIT;
-  if (split < 1u) split = 1u;
-  // round the split up to a supported instantiation
-  split = split <= 1u ? 1u : split <= 2u ? 2u : split <= 4u ? 4u : 8u;
-  p.split = split;
-  p.ks = (KT + split - 1u) / split;
-  if (p.ks < 1u) p.ks = 1u;
-  return p;
+// Which activation staging fits (or -1: the decode kernel does not apply).
+static int gemv_amode(int64_t M, int64_t K) {
+  const int64_t KT = (K + 255) / 256, Kp = KT * 256;
+  const int64_t af16 = M * (2 * Kp + 16) + 512;
+  const int64_t af16_chunks = M * (Kp / 32);
+  if (af16 <= (int64_t)GV_A_BYTES && af16_chunks <= 1024 * (int64_t)GV_A_LOADS_F16) return kAF16;
+  if (KT * 4608 <= (int64_t)GV_A_BYTES && KT * 256 <= 1024 * (int64_t)GV_A_LOADS_CODE && KT * 32 <= 1024)
+    return kACode;
+  return -1;
 }
 
 }  // namespace
 
-// Decode-path workspace: GV_COUNTER_BYTES of per-column-block counters at the
-// start (zero before and after every call, at the same place whatever the
-// shape), then the split-K partial sums (scratch).
-constexpr size_t GV_COUNTER_BYTES = 65536;
-constexpr int64_t GV_MAX_N = (int64_t)(GV_COUNTER_BYTES / sizeof(uint32_t)) * GV_ROWS;
-
-size_t gemv_nv_workspace(int64_t M, int64_t N, int64_t K) {
-  if (M > 32 || M <= 0 || N <= 0 || N > GV_MAX_N) return 0;
-  const GemvPlan p = gemv_plan(N, K);
-  return GV_COUNTER_BYTES + (size_t)p.ks * (size_t)M * (size_t)N * sizeof(float);
+bool gemv_nv_applies(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 32 && N >= 1 && gemv_amode(M, K) >= 0;
 }
-
-template <int OUT>
-static void launch_gemv(const GemvPlan& p, dim3 grid, const uint8_t* A, const uint8_t* sA, const uint8_t* W,
-                        const uint8_t* sW, const float* tsA, const float* tsW, void* C, float* partial,
-                        uint32_t* counters, uint32_t M, uint32_t N, uint32_t K, hipStream_t stream) {
-  switch (p.split) {
-    case 1: gemv_nv_kernel<OUT, 1><<<grid, 256, 0, stream>>>(A, sA, W, sW, tsA, tsW, C, partial, counters, M, N, K, p.ks); break;
-    case 2: gemv_nv_kernel<OUT, 2><<<grid, 256, 0, stream>>>(A, sA, W, sW, tsA, tsW, C, partial, counters, M, N, K, p.ks); break;
-    case 4: gemv_nv_kernel<OUT, 4><<<grid, 256, 0, stream>>>(A, sA, W, sW, tsA, tsW, C, partial, counters, M, N, K, p.ks); break;
-    default: gemv_nv_kernel<OUT, 8><<<grid, 256, 0, stream>>>(A, sA, W, sW, tsA, tsW, C, partial, counters, M, N, K, p.ks); break;
-  }
-}
-
-bool gemv_nv_applies(int64_t M, int64_t N) { return M >= 1 && M <= 32 && N <= GV_MAX_N; }
 
 hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
-                          int out_dtype, void* workspace, hipStream_t stream) {
-  const GemvPlan p = gemv_plan(N, K);
-  uint32_t* counters = static_cast<uint32_t*>(workspace);
-  float* partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + GV_COUNTER_BYTES);
-  const dim3 grid(p.nblocks * p.ks);
-  if (out_dtype == 0)
-    launch_gemv<0>(p, grid, A, sA, B, sB, tsA, tsB, C, partial, counters, (uint32_t)M, (uint32_t)N, (uint32_t)K,
-                   stream);
-  else
-    launch_gemv<1>(p, grid, A, sA, B, sB, tsA, tsB, C, partial, counters, (uint32_t)M, (uint32_t)N, (uint32_t)K,
-                   stream);
+                          int out_dtype, hipStream_t stream) {
+  const uint32_t nblocks = (uint32_t)((N + 31) / 32);
+  const dim3 grid(nblocks < 256u ? nblocks : 256u);
+  const dim3 block(GV_WAVES * 64);
+  const uint32_t m = (uint32_t)M, n = (uint32_t)N, k = (uint32_t)K;
+  const int mode = gemv_amode(M, K);
+  if (mode == kAF16) {
+    if (out_dtype == 0) gemv_nv_kernel<kAF16, 0><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+    else gemv_nv_kernel<kAF16, 1><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+  } else {
+    if (out_dtype == 0) gemv_nv_kernel<kACode, 0><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+    else gemv_nv_kernel<kACode, 1><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+  }
   return hipGetLastError();
 }
 

@@ -97,13 +97,14 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
 
 /* Workspace bytes an operation needs (0 if none).  For FP4_OP_QUANTIZE, M is
  * the row count; for FP4_OP_GEMM_GROUPED, E is the expert count and M the total
- * routed rows.  Operations keep their control words (completion counters) at
- * the start of the workspace and scratch data after them.  A workspace must be
- * zero-filled once before its first use; every call leaves the control words
- * zero again when its work on the stream completes, so one zero-filled
- * workspace of the largest size needed serves any sequence of calls.  Calls
- * that share one workspace must be ordered (same stream, or events); calls
- * that overlap on one workspace race.  Host-only. */
+ * routed rows.  Today only NVFP4 quantisation that computes its own tensor
+ * scale needs one (8 bytes: the running amax and a completion counter); GEMMs
+ * return 0.  Operations keep their control words at the start of the
+ * workspace.  A workspace must be zero-filled once before its first use; every
+ * call leaves the control words zero again when its work on the stream
+ * completes, so one zero-filled workspace of the largest size needed serves
+ * any sequence of calls.  Calls that share one workspace must be ordered (same
+ * stream, or events); calls that overlap on one workspace race.  Host-only. */
 size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E);
 
 /* Quantise a rows x K matrix x (K contiguous) of `in_dtype` (FP32 or BF16).
@@ -141,8 +142,12 @@ int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const floa
  *   MXFP4 runs on the gfx950 block-scaled FP4 matrix core with the E8M0 scales
  *   applied inside the instruction; NVFP4 decodes E2M1 * E4M3 exactly to FP16
  *   and runs the FP16 matrix core, with the tensor scales in the epilogue.
- *   NVFP4 with M <= 32 (decode shapes) takes a bandwidth-first path that splits
- *   K across workgroups and needs the workspace for its partial sums.
+ *   NVFP4 with M <= 32 (decode shapes) takes a bandwidth-first path: one
+ *   workgroup per 32 weight rows, K split over its wavefronts and summed in a
+ *   fixed order (results do not depend on timing); no workspace.  It applies
+ *   while the activation fits the workgroup's staging memory (for example
+ *   M <= 8 with K <= 8960, or any M <= 32 with K <= 8192); larger shapes take
+ *   the tiled kernel.
  * Requirements: K % 32 == 0 (both formats); codes 16-byte aligned; scales
  *   4-byte aligned; C aligned to its element size.  M, N >= 0 arbitrary.
  *   workspace: fp4_workspace_size(FP4_OP_GEMM, fmt, M, N, K, 0) bytes,
@@ -163,8 +168,9 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
  *   (A[row_idx[r]] . B_e^T) * tsA * tsB for its expert e.
  *   Group sizes stay on the device; the kernel builds its own tile list.
  *   Every row_idx entry must lie in [0, A_rows).
+ * Formats: FP4_MXFP4 and FP4_MXFP4_OCP; FP4_NVFP4 returns FP4_ERR_FMT.
  * Requirements as fp4_gemm; workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
- *   fmt, total_rows, N, K, E) bytes. */
+ *   fmt, total_rows, N, K, E) bytes (0 today). */
 int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                      const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
                      const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N, int64_t K,

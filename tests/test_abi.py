@@ -61,6 +61,8 @@ def test_workspace_sizes(L):
     assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.MXFP4, 10, 0, 64) == 0
     assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.NVFP4, 10, 0, 64) == 8
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.MXFP4, 8192, 8192, 8192) == 0
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 1, 8192, 8192) == 0
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 8192, 8192) == 0
 
 
 FAKE = 0x100000  # 16-byte-aligned fake device address: never dereferenced on the error paths

@@ -157,6 +157,28 @@ def test_closed_forms_bit_exact(orc, fmt):
         np.testing.assert_array_equal(C, ref)
 
 
+@pytest.mark.parametrize("M", [5, 20, 40])
+def test_nvfp4_every_e4m3_scale_byte(orc, M):
+    """Every finite E4M3 byte as a block scale of A and of B, exactly: W row n
+    holds 1.0 codes only in block n, with scale byte n; A row m holds 1.0 codes
+    with scale byte (7m + 13b) mod 127 in block b; so C[m, n] = 16 * e4m3(sA) *
+    e4m3(n), a product exact in FP32.  M = 5 and 20 take the decode kernel's two
+    activation stagings, M = 40 the tiled GEMM."""
+    fmt, N, K = 1, 127, 2048
+    A = np.full((M, K), 2, np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        B[n, 16 * n:16 * n + 16] = 2
+    sa = lambda r, b: (7 * r + 13 * b) % 127
+    sA = _scales(orc, fmt, M, K, sa)
+    sB = _scales(orc, fmt, N, K, lambda r, b: r if b == r else 0x38)
+    say("every e4m3 byte M=%d" % M)
+    C = _run_raw(fmt, _pack(A), sA, _pack(B), sB, M, N, K, 1.0, 1.0)
+    want = np.array([[16.0 * orc.e4m3_value(sa(m, n)) * orc.e4m3_value(n) for n in range(N)] for m in range(M)],
+                    np.float32)
+    np.testing.assert_array_equal(C, want)
+
+
 def test_exact_small_exponent_range_bit_exact(orc):
     """Scale exponents within a range of 4 and K <= 256 keep every partial sum
     exact in FP32, so any accumulation order gives the oracle's value."""
@@ -218,31 +240,67 @@ def test_nvfp4_mlp_sampled(orc):
     assert_gemm_close(orc, Cs, Cref, T, True, "nvfp4_mlp sampled")
 
 
+# Activation staged as FP16 (M x K small), as codes (larger), or too large for
+# the decode kernel (the tiled GEMM takes it): (8, 100, 8960) is the largest
+# FP16 staging at M = 8, (32, 130, 8192) the largest code staging.
 @pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (17, 256, 4096), (32, 130, 8192),
-                                   (1, 8192, 256), (32, 64, 96)])
+                                   (1, 8192, 256), (32, 64, 96), (8, 100, 8960), (9, 100, 8192), (32, 64, 8448),
+                                   (2, 64, 40000)])
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_nvfp4_decode_gemv(orc, M, N, K, bf16_out):
-    """M <= 32 rows take the decode kernel (split-K partials, last-workgroup
-    reduction); checked in full against the oracle."""
+    """M <= 32 rows take the decode kernel (K split over the workgroup's
+    waves, reduced in LDS); checked in full against the oracle."""
     _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 13 + N + K, a_std=1.0, b_std=0.02)
 
 
 def test_nvfp4_decode_gemv_repeated_calls(orc):
-    """The split-K counters reset themselves: the same workspace serves
-    several calls in a row (and a smaller problem after a larger one)."""
+    """The decode kernel keeps no state and needs no workspace: several calls
+    in a row (a smaller problem after a larger one) all agree with the oracle."""
     import block_scaled_fp4_03_amd as fp4
     import torch
     K = 2048
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 1024, K) == 0
     w = synth.gaussian(71, (1024, K), std=0.02, bernoulli=0.001)
     qw, rw = _quant_both(orc, w, 1)
-    ws = torch.zeros(fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 1024, K), dtype=torch.uint8, device="cuda")
     for M in (32, 8, 1, 32):
         x = synth.to_bf16_bits(synth.gaussian(72 + M, (M, K)))
         qx, rx = _quant_both(orc, x, 1)
         say("gemv repeated M=%d" % M)
-        C = fp4.gemm(qx, qw, out_dtype=torch.float32, ws=ws)
+        C = fp4.gemm(qx, qw, out_dtype=torch.float32)
         Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, 1024, K, 1, tsA=rx[3], tsB=rw[3])
         assert_gemm_close(orc, to_host(C), Cref, T, False, "gemv repeated M=%d" % M)
+
+
+def test_nvfp4_decode_many_row_blocks(orc):
+    """More 32-row weight blocks than the decode grid holds (grid-stride loop),
+    a ragged last block and a ragged K tail."""
+    import torch
+    M, N, K = 3, 1024 * 32 + 40, 288
+    a = synth.gaussian(81, (M, K))
+    b = synth.gaussian(82, (N, K), std=0.02, bernoulli=0.002)
+    say("gemv many row blocks M=%d N=%d K=%d" % (M, N, K))
+    qa, ra = _quant_both(orc, a, 1)
+    qb, rb = _quant_both(orc, b, 1)
+    import block_scaled_fp4_03_amd as fp4
+    C = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, 1, tsA=ra[3], tsB=rb[3])
+    assert_gemm_close(orc, to_host(C), Cref, T, False, "gemv many row blocks")
+
+
+@pytest.mark.parametrize("fmt,M", [(1, 1), (1, 32), (0, 4), (0, 300)])
+def test_gemm_k_zero(fmt, M):
+    """K == 0: the product is empty and C is all zeros."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    N = 70
+    say("gemm K=0 fmt=%d M=%d" % (fmt, M))
+    ts = torch.ones(1, dtype=torch.float32, device="cuda") if fmt == 1 else None
+    e = torch.empty(0, dtype=torch.uint8, device="cuda")
+    qa = fp4.Quantized(e, e, ts, fmt, M, 0)
+    qb = fp4.Quantized(e, e, ts, fmt, N, 0)
+    C = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    fp4.gemm(qa, qb, out=C)
+    assert (to_host(C) == 0).all()
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])

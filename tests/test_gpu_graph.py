@@ -1,0 +1,98 @@
+"""Quantise + GEMM steps captured in a HIP graph: every replay (with eager work
+and synchronisations in between) must reproduce the eager result bit for bit,
+and the eager result must agree with the oracle.  The NVFP4 step includes the
+tensor-amax reduction and the decode GEMV, both of which keep self-resetting
+counters in the workspace, so a replay that saw stale counters would differ."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import assert_gemm_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(step, n):
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            step()
+    torch.cuda.synchronize()
+    return g
+
+
+def _replay_and_check(g, out, ref, eager_noise):
+    import torch
+    for rep in range(4):
+        out.zero_()
+        eager_noise()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), "replay %d differs from eager" % rep
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_graph_nvfp4_decode(orc, M):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    N, K = 1024, 2048
+    w = synth.gaussian(2, (N, K), std=0.02, bernoulli=0.001)
+    x = synth.to_bf16_bits(synth.gaussian(202 + M, (M, K)))
+    say("graph nvfp4 decode M=%d N=%d K=%d" % (M, N, K))
+    qw = fp4.quantize(to_dev(w), fp4.NVFP4)
+    xd = to_dev(x)
+    qx = fp4.quantize(xd, fp4.NVFP4)
+    wsq = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, M, 0, K)
+    wsg = fp4.workspace(fp4.OP_GEMM, fp4.NVFP4, M, N, K)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        fp4.quantize(xd, fp4.NVFP4, ws=wsq, out=qx)
+        fp4.gemm(qx, qw, out=C, ws=wsg)
+
+    step()
+    torch.cuda.synchronize()
+    ref = C.clone()
+    rx = orc.quantize(x, orc.FMT_NVFP4)
+    rw = orc.quantize(w, orc.FMT_NVFP4)
+    np.testing.assert_array_equal(to_host(qx.codes), rx[0])
+    Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, N, K, orc.FMT_NVFP4, tsA=rx[3], tsB=rw[3])
+    assert_gemm_close(orc, to_host(C), Cref, T, True, "eager decode M=%d" % M)
+
+    g = _capture(step, 3)
+    other = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    _replay_and_check(g, C, ref, lambda: fp4.gemm(fp4.quantize(other, fp4.NVFP4), qw))
+
+
+def test_graph_mxfp4_small(orc):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    a, b = synth.mxfp4_256()
+    say("graph mxfp4 256^3")
+    xa, xb = to_dev(a), to_dev(b)
+    qa, qb = fp4.quantize(xa, fp4.MXFP4), fp4.quantize(xb, fp4.MXFP4)
+    C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp4.quantize(xa, fp4.MXFP4, out=qa)
+        fp4.quantize(xb, fp4.MXFP4, out=qb)
+        fp4.gemm(qa, qb, out=C)
+
+    step()
+    torch.cuda.synchronize()
+    ref = C.clone()
+    ra, rb = orc.quantize(a, orc.FMT_MXFP4), orc.quantize(b, orc.FMT_MXFP4)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], 256, 256, 256, orc.FMT_MXFP4)
+    assert_gemm_close(orc, to_host(C), Cref, T, False, "eager 256^3")
+
+    g = _capture(step, 2)
+    other = torch.randn(256, 256, device="cuda")
+    _replay_and_check(g, C, ref, lambda: fp4.gemm(fp4.quantize(other, fp4.MXFP4), qb))
