@@ -82,12 +82,17 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
+    // Device-scope atomics meet at one coherence point for all XCDs.  The max
+    // must be performed before this block counts itself in, so wait for its
+    // return before the add; the block that counts last then reads the final
+    // max.  (A release fence here would write back and invalidate the XCD's
+    // whole L2 once per block.)
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(&ws[0], f2u(m));
-    __threadfence();
-    uint32_t done = atomicAdd(&ws[1], 1u);
+    const uint32_t prev = __hip_atomic_fetch_max(&ws[0], f2u(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" : : "v"(prev) : "memory");
+    const uint32_t done = __hip_atomic_fetch_add(&ws[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x - 1) {
-      float amax = u2f(atomicOr(&ws[0], 0u));
+      const float amax = u2f(__hip_atomic_fetch_or(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       float s = 1.0f;
       if (amax > 0.0f) {
         s = amax / 2688.0f;
