@@ -27,7 +27,8 @@
 // chunk parity + row, ds_read_b128) are free of bank conflicts while each
 // load instruction still reads 8 whole 128-byte row segments.  Within a stage,
 // the operands of the next 64-value sub-step are read while the current one
-// multiplies; one barrier per stage.
+// multiplies; one barrier per stage.  The epilogue goes through LDS so that C
+// is written with 16-byte row-contiguous stores.
 //
 // Grouped: the tiles of all experts form one list, ordered expert by expert;
 // every workgroup derives its (expert, m-tile, n-tile) from the device-side
@@ -369,9 +370,62 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   }
 
   // ---- epilogue: x tsA * tsB, FP32 or BF16 (round to nearest even).  Lane L
-  // of a 32x32 block holds column L%32, rows 8*(i/4) + 4*(L/32) + i%4.
+  // of a 32x32 block holds column L%32, rows 8*(i/4) + 4*(L/32) + i%4.  The
+  // tile goes through LDS (free once every wave is past its last stage) so
+  // that global stores are 16-byte, row-contiguous; BF16 in one pass, FP32 in
+  // two passes of 128 rows.  A row pitch of C that is not a multiple of 16
+  // bytes, or an unaligned C, takes per-element stores.
   const float scale = (tsA ? *tsA : 1.0f) * (tsB ? *tsB : 1.0f);
   const size_t crow0 = (size_t)row0 + m0;
+  constexpr uint32_t EB = OUT == 0 ? 4u : 2u;              // bytes per element
+  constexpr uint32_t PASS_ROWS = OUT == 0 ? 128u : 256u;    // tile rows per pass
+  constexpr uint32_t LROW = BN * EB + 16u;                  // LDS row pitch (bank shift of 4 per row)
+  static_assert(PASS_ROWS * LROW <= NSTAGE * STAGE_BYTES, "epilogue tile must fit in LDS");
+  const bool vec_ok = ((N * EB) % 16u == 0u) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0u);
+  // No copy into LDS may still be in flight when LDS is reused or released
+  // (the last loop iterations copy zero-filled stages past K).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (vec_ok) {
+    __syncthreads();
+#pragma unroll
+    for (uint32_t pass = 0; pass < 256u / PASS_ROWS; ++pass) {
+      if (PASS_ROWS == 256u || wm == pass) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint32_t lcol = 64u * wn + 32u * c + li;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t lrow = (PASS_ROWS == 256u ? 128u * wm : 0u) + 32u * r + 8u * (i >> 2) + 4u * lj + (i & 3);
+              const float v = acc[r][c][i] * scale;
+              if (OUT == 0)
+                *reinterpret_cast<float*>(lds + lrow * LROW + 4u * lcol) = v;
+              else
+                *reinterpret_cast<uint16_t*>(lds + lrow * LROW + 2u * lcol) = f32_to_bf16(v);
+            }
+          }
+      }
+      __syncthreads();
+      // 16-byte chunks: BN * EB / 16 per row; 512 threads cover 512 chunks per step.
+      constexpr uint32_t CPR = BN * EB / 16u;
+      constexpr uint32_t STEPS = PASS_ROWS * CPR / 512u;
+#pragma unroll
+      for (uint32_t st = 0; st < STEPS; ++st) {
+        const uint32_t q = st * 512u + threadIdx.x;
+        const uint32_t lrow = q / CPR, ch = q % CPR;
+        const uint32_t row = pass * PASS_ROWS + lrow;
+        const uint32_t col = n0 + ch * (16u / EB);
+        // N * EB is a multiple of 16 and col a multiple of 16 / EB, so a chunk
+        // that starts inside the row lies wholly inside it.
+        if (row < rowsA && col < N)
+          *reinterpret_cast<v4i*>(static_cast<uint8_t*>(C) + ((crow0 + row) * N + col) * EB) =
+              *reinterpret_cast<const v4i*>(lds + lrow * LROW + 16u * ch);
+      }
+      if (PASS_ROWS != 256u) __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
 #pragma unroll
