@@ -13,7 +13,9 @@ workload, and, under "workloads", the other measured workloads:
 
   nvfp4_decode_m{1,8,32}  W 8192x8192 NVFP4 (pre-quantised), X Mx8192 BF16
                           quantised on the fly; step = tensor amax + quantise
-                          + decode GEMV; GB/s of algorithmic bytes vs 8 TB/s.
+                          + decode GEMV (one fused kernel at M = 1, three
+                          kernels at M = 8, 32); GB/s of algorithmic bytes vs
+                          8 TB/s.
   nvfp4_mlp               A 4096x4096 BF16 quantised on the fly, W 14336x4096
                           NVFP4; step = amax + quantise + GEMM; TFLOP/s.
   mxfp4_moe               32 experts 5760x2880 MXFP4, 16384 BF16 tokens
@@ -178,14 +180,23 @@ def nvfp4_decode(torch, fp4, synth, M):
     qw = [qw0] + [fp4.Quantized(qw0.codes.clone(), qw0.scales.clone(), qw0.tensor_scale.clone(), fp4.NVFP4, N, K)
                   for _ in range(ROTATE - 1)]
     x = to_dev(torch, synth.nvfp4_decode_act(M))
-    qx = fp4.quantize(x, fp4.NVFP4)  # output buffers reused by every step
-    wsq = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, M, 0, K)
-    wsg = fp4.workspace(fp4.OP_GEMM, fp4.NVFP4, M, N, K)
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    # The one-kernel path re-quantises X in every workgroup; it beats the
+    # three-kernel step at small M only (measured: M = 1 16.3 vs 18.4 us,
+    # M = 8 22.3 vs 21.3 us).
+    fused = M <= 4 and bool(fp4.fp4_gemm_nvfp4_act_supported(M, N, K, fp4.BF16))
+    if fused:
+        # one kernel: tensor amax + NVFP4 quantise of X + GEMV
+        def step(i):
+            fp4.gemm_nvfp4_act(x, qw[i % ROTATE], out=C)
+    else:
+        qx = fp4.quantize(x, fp4.NVFP4)  # output buffers reused by every step
+        wsq = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, M, 0, K)
+        wsg = fp4.workspace(fp4.OP_GEMM, fp4.NVFP4, M, N, K)
 
-    def step(i):
-        fp4.quantize(x, fp4.NVFP4, ws=wsq, out=qx)
-        fp4.gemm(qx, qw[i % ROTATE], out=C, ws=wsg)
+        def step(i):
+            fp4.quantize(x, fp4.NVFP4, ws=wsq, out=qx)
+            fp4.gemm(qx, qw[i % ROTATE], out=C, ws=wsg)
 
     step(0)
     torch.cuda.synchronize()
@@ -202,7 +213,8 @@ def nvfp4_decode(torch, fp4, synth, M):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"M": M, "N": N, "K": K, "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": int(nbytes),
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "step": "tensor amax + NVFP4 quantise of X + decode GEMV (HIP graph replay)"}
+            "step": ("one kernel: tensor amax + NVFP4 quantise of X + decode GEMV" if fused else
+                     "three kernels: tensor amax, NVFP4 quantise of X, decode GEMV") + " (HIP graph replay)"}
 
 
 def nvfp4_mlp(torch, fp4, synth):

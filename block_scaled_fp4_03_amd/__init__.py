@@ -22,7 +22,7 @@ OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 TS_GIVEN = 1
 
 FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_dequantize", "fp4_gemm",
-             "fp4_gemm_grouped", "fp4_status_string")
+             "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -49,6 +49,8 @@ def lib():
             "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
             "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_grouped": (I32, [P, P, I64, P, P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
+            "fp4_gemm_nvfp4_act": (I32, [P, I32, P, U32, P, P, P, P, I64, I64, I64, I32, P]),
+            "fp4_gemm_nvfp4_act_supported": (I32, [I64, I64, I64, I32]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
         }
         for name, (res, args) in sig.items():
@@ -90,6 +92,14 @@ def fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, t
                      workspace, workspace_bytes, stream):
     return lib().fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, total_rows, N, K, fmt,
                                   out_dtype, workspace, workspace_bytes, stream)
+
+
+def fp4_gemm_nvfp4_act(X, x_dtype, x_tensor_scale, flags, W, sW, tsW, C, M, N, K, out_dtype, stream):
+    return lib().fp4_gemm_nvfp4_act(X, x_dtype, x_tensor_scale, flags, W, sW, tsW, C, M, N, K, out_dtype, stream)
+
+
+def fp4_gemm_nvfp4_act_supported(M, N, K, x_dtype):
+    return lib().fp4_gemm_nvfp4_act_supported(M, N, K, x_dtype)
 
 
 # ---- torch helpers: allocation + pointer/stream marshalling only -------------
@@ -206,4 +216,24 @@ def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_s
                           _ptr(b_scales), _ptr(a.tensor_scale), _ptr(b_tensor_scale), _ptr(out), total, N, K, fmt,
                           _dtype_code(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "fp4_gemm_grouped")
+    return out
+
+
+def gemm_nvfp4_act(x, w, tensor_scale=None, ts_out=None, out_dtype=None, out=None, stream=None):
+    """C = quantise_nvfp4(x) . w^T in one call (see fp4_gemm_nvfp4_act in
+    include/fp4.h).  x: M x K float32/bfloat16 CUDA tensor; w: NVFP4 Quantized.
+    tensor_scale: given activation tensor scale (1-element float32 tensor), or
+    None to compute it; ts_out: optional 1-element tensor receiving it."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.rows
+    if w.K != K or w.fmt != NVFP4:
+        raise ValueError("weights must be NVFP4 with the same K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=x.device)
+    flags = TS_GIVEN if tensor_scale is not None else 0
+    ts = tensor_scale if tensor_scale is not None else ts_out
+    rc = fp4_gemm_nvfp4_act(_ptr(x), _dtype_code(x), _ptr(ts), flags, _ptr(w.codes), _ptr(w.scales),
+                            _ptr(w.tensor_scale), _ptr(out), M, N, K, _dtype_code(out), _stream(stream))
+    _check(rc, "fp4_gemm_nvfp4_act")
     return out

@@ -24,6 +24,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFmtMX = 0, kFmtNV = 1, kFmtMXOcp = 2;
 
+// Input / output element types (the C ABI's fp4_dtype values).
+constexpr int kDtF32 = 0, kDtBF16 = 1;
+
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
@@ -114,6 +117,40 @@ __device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
 __device__ __forceinline__ v2h scale_pair(uint32_t b) {
   const uint32_t h = e4m3_to_f16_bits(b);
   return __builtin_bit_cast(v2h, h | (h << 16));
+}
+
+// Eight already-scaled values to eight E2M1 codes (element 2i in the low
+// nibble of byte i).  The gfx950 converter rounds x/1.0 to the nearest E2M1
+// value, ties to even, saturating at +-6, and keeps the sign (so -0 and
+// negative values that round to zero give code 8).
+__device__ __forceinline__ uint32_t pack8(const float y[8]) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
+  return r;
+}
+
+// x / d rounded to nearest even, for the 16 elements of an NVFP4 block that
+// share d (finite, > 0) and rd = 1.0f / d (correctly rounded).  For
+// d >= 2^-100: q = RN(|x| * rd) is within a few ulps of |x| / d; each step
+// q + RN(|x| - q * d) * rd (the remainder is exact in one FMA) is Markstein's
+// correction, and the second one starts from a faithful q, so it returns the
+// correctly rounded quotient (no underflow: the quotients that matter,
+// >= 0.25, have |x| >= 2^-102).  Tiny d takes the plain division.  The sign
+// is copied, so -0 stays -0.
+__device__ __forceinline__ float nv_div(float x, float d, float rd) {
+  const float a = __builtin_fabsf(x);
+  float q;
+  if (d >= 7.888609052210118e-31f) {  // 2^-100
+    q = a * rd;
+    q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
+    q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
+  } else {
+    q = a / d;
+  }
+  return __builtin_copysignf(q, x);
 }
 
 // Two E4M3 bytes (bits 0-15 of w, or 16-31 when HI) as two FP16 values: the

@@ -36,4 +36,10 @@ hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                           int out_dtype, hipStream_t stream);
 
+// The same with the activation quantised inside the kernel (small M x K).
+bool gemv_nv_fused_applies(int64_t M, int64_t N, int64_t K, int x_dtype);
+hipError_t launch_gemv_nv_fused(const void* X, int x_dtype, float* x_tensor_scale, unsigned flags,
+                                const uint8_t* B, const uint8_t* sB, const float* tsB, void* C, int64_t M,
+                                int64_t N, int64_t K, int out_dtype, hipStream_t stream);
+
 }  // namespace fp4

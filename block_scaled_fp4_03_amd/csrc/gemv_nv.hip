@@ -6,6 +6,8 @@
 // Decoding streams every weight once, so the path is bound by HBM bandwidth
 // ("Rubin FP4 GEMM deep dive", §1.2, §6.2); operands are decoded exactly to
 // FP16 and multiplied on the FP16 matrix core (see gemm.hip for why FP16).
+#include <float.h>
+
 #include "fp4_launch.h"
 #include "gemm_common.h"
 
@@ -41,25 +43,35 @@ namespace {
 // workspace.
 // ---------------------------------------------------------------------------
 constexpr uint32_t GV_WAVES = 16;               // wavefronts per workgroup (K split)
-constexpr uint32_t GV_PD = 1;                   // weight tiles in flight per wave
+// Weight tiles in flight per wave (ring depth), both paths.  Depth 1 measured
+// best also for the fused path: with depth 2 the whole weight matrix is asked
+// for at once and the main loop starts later (M = 1: 16.3 -> 20.8 us, M = 8:
+// 22.3 -> 30.0 us at 8192 x 8192).
+#define GV_FUSED_PD 1
 constexpr uint32_t GV_RED_BYTES = 4u * 32u * 32u * 4u;         // 4 partial-sum slots
 constexpr uint32_t GV_A_BYTES = 160u * 1024u - GV_RED_BYTES;    // activation staging
 // 16-byte activation loads per thread (at most): FP16 staging, code staging.
 constexpr uint32_t GV_A_LOADS_F16 = 3;
 constexpr uint32_t GV_A_LOADS_CODE = 8;
 
-enum { kAF16 = 0, kACode = 1 };
+// Fused: the activation arrives unquantised (FP32 or BF16); every workgroup
+// takes its maximum and quantises it itself (the same NVFP4 steps as the
+// quantiser), staging the exact FP16 values as in kAF16.  X blocks per thread.
+constexpr uint32_t GV_X_BLOCKS_BF16 = 4;
+constexpr uint32_t GV_X_BLOCKS_F32 = 2;
+
+enum { kAF16 = 0, kACode = 1, kFused = 2 };
 
 struct GvTile {
   v4i w[4];   // codes: 32 values per lane per 64-value sub-step
   u32x2 ws;   // the lane's 8 scale bytes (4 sub-steps x 2 blocks)
 };
 
-template <int AMODE, int OUT>
+template <int AMODE, int OUT, int XDT, int PD>
 __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const uint8_t* __restrict__ W,
     const uint8_t* __restrict__ sW, const float* __restrict__ tsA, const float* __restrict__ tsW, void* __restrict__ C,
-    uint32_t M, uint32_t N, uint32_t K) {
+    uint32_t M, uint32_t N, uint32_t K, const void* __restrict__ X, float* __restrict__ ts_out, uint32_t flags) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[GV_A_BYTES];
   __shared__ float red[4][32][32];
 
@@ -82,41 +94,63 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
   // ---- activation loads (issued before the weights: waits are in order)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, M * ldb);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sA, srow);
-  constexpr int NA = AMODE == kAF16 ? (int)GV_A_LOADS_F16 : (int)GV_A_LOADS_CODE;
+  constexpr int NA = AMODE == kACode ? (int)GV_A_LOADS_CODE : AMODE == kAF16 ? (int)GV_A_LOADS_F16 : 1;
   v4i ald[NA];
   uint32_t asc[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const uint32_t c = tid + 1024u * i;   // 16-byte chunk handled by this thread
-    uint32_t off = 0x80000000u, soff = 0x80000000u;
-    if (AMODE == kAF16) {
-      const uint32_t cpr = Kp / 32u;       // chunks per row
-      const uint32_t row = c / cpr, cc = c % cpr;
-      if (row < M && cc * 16u < ldb) {
-        off = row * ldb + cc * 16u;
-        soff = scale_offset<kFmtNV>(row, 2u * cc, KT);
-      }
-      asc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
-    } else {
-      if (c < KT * 256u) {                  // operand-order chunk: tile, sub-step, lane
-        const uint32_t blk = c >> 6, L = c & 63u;
-        const uint32_t row = L & 31u;
-        if (row < M) off = row * ldb + (blk >> 2) * 128u + (blk & 3u) * 32u + 16u * (L >> 5);
-      }
-    }
-    ald[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-  }
   v4i ascl = v4i{};
-  if (AMODE == kACode) {
-    // scale tiles verbatim: KT x 512 B = KT * 32 chunks (<= 1 per thread for KT <= 32)
-    const uint32_t c = tid;
-    ascl = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsa, c < KT * 32u ? c * 16u : 0x80000000u, 0, 0));
+  // Fused: 16-value blocks of X (rows < M, K padded to Kp with zeros); block
+  // b = tid + 1024 i is row b / (Kp/16), block b % (Kp/16) of that row.
+  constexpr uint32_t XEB = XDT == kDtBF16 ? 2u : 4u;              // bytes per X value
+  constexpr int XNB = AMODE == kFused ? (XDT == kDtBF16 ? (int)GV_X_BLOCKS_BF16 : (int)GV_X_BLOCKS_F32) : 1;
+  constexpr int XLPB = (int)(16u * XEB / 16u);                     // 16-byte loads per block
+  v4i xl[XNB][XLPB];
+  const uint32_t xbpr = Kp / 16u;                                   // blocks per (padded) row
+  if (AMODE != kFused) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const uint32_t c = tid + 1024u * i;   // 16-byte chunk handled by this thread
+      uint32_t off = 0x80000000u, soff = 0x80000000u;
+      if (AMODE == kAF16) {
+        const uint32_t cpr = Kp / 32u;       // chunks per row
+        const uint32_t row = c / cpr, cc = c % cpr;
+        if (row < M && cc * 16u < ldb) {
+          off = row * ldb + cc * 16u;
+          soff = scale_offset<kFmtNV>(row, 2u * cc, KT);
+        }
+        asc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
+      } else {
+        if (c < KT * 256u) {                  // operand-order chunk: tile, sub-step, lane
+          const uint32_t blk = c >> 6, L = c & 63u;
+          const uint32_t row = L & 31u;
+          if (row < M) off = row * ldb + (blk >> 2) * 128u + (blk & 3u) * 32u + 16u * (L >> 5);
+        }
+      }
+      ald[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+    }
+    if (AMODE == kACode) {
+      // scale tiles verbatim: KT x 512 B = KT * 32 chunks (<= 1 per thread for KT <= 32)
+      const uint32_t c = tid;
+      ascl = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rsa, c < KT * 32u ? c * 16u : 0x80000000u, 0,
+                                                                          0));
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, M * K * XEB);
+#pragma unroll
+    for (int i = 0; i < XNB; ++i) {
+      const uint32_t b = tid + 1024u * i;
+      const uint32_t row = b / xbpr, bk = b % xbpr;
+      const bool ok = row < M && 16u * bk < K;
+#pragma unroll
+      for (int l = 0; l < XLPB; ++l)
+        xl[i][l] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (row * K + 16u * bk) * XEB + 16u * l : 0x80000000u, 0, 0));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- weight ring prologue
   const uint32_t lane_off = li * ldb + 16u * lj;
-  GvTile ring[GV_PD];
+  GvTile ring[PD];
   auto issue = [&](GvTile& d, uint32_t j) {
     const uint32_t rb = blockIdx.x + (j / NJ) * gridDim.x;
     const uint32_t kt = wave + GV_WAVES * (j % NJ);
@@ -134,39 +168,111 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
                                                                           0, 0));
   };
 #pragma unroll
-  for (int p = 0; p < (int)GV_PD; ++p)
+  for (int p = 0; p < PD; ++p)
     if ((uint32_t)p < T) issue(ring[p], p);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- activation -> LDS
+  float s_x = 1.0f;   // activation tensor scale (fused)
+  if (AMODE != kFused) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const uint32_t c = tid + 1024u * i;
-    if (AMODE == kAF16) {
-      const uint32_t cpr = Kp / 32u;
-      const uint32_t row = c / cpr, cc = c % cpr;
-      if (row < M) {
-        const v2h s0 = scale_pair(asc[i] & 0xFFu), s1 = scale_pair((asc[i] >> 8) & 0xFFu);
-        uint8_t* dst = lds_a + row * RS + cc * 64u;
+    for (int i = 0; i < NA; ++i) {
+      const uint32_t c = tid + 1024u * i;
+      if (AMODE == kAF16) {
+        const uint32_t cpr = Kp / 32u;
+        const uint32_t row = c / cpr, cc = c % cpr;
+        if (row < M) {
+          const v2h s0 = scale_pair(asc[i] & 0xFFu), s1 = scale_pair((asc[i] >> 8) & 0xFFu);
+          uint8_t* dst = lds_a + row * RS + cc * 64u;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<v8h*>(dst + 16u * g) = decode8((uint32_t)ald[i][g], g < 2 ? s0 : s1);
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<v8h*>(dst + 16u * g) = decode8((uint32_t)ald[i][g], g < 2 ? s0 : s1);
+        }
+      } else {
+        if (c < KT * 256u) *reinterpret_cast<v4i*>(lds_a + 16u * c) = ald[i];
       }
+    }
+    if (AMODE == kACode && tid < KT * 32u) *reinterpret_cast<v4i*>(lds_a + KT * 4096u + 16u * tid) = ascl;
+  } else {
+    // The block's 16 values, FP32.
+    float xv[XNB][16];
+#pragma unroll
+    for (int i = 0; i < XNB; ++i)
+#pragma unroll
+      for (int l = 0; l < XLPB; ++l)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = (uint32_t)xl[i][l][e];
+          if (XDT == kDtBF16) {
+            xv[i][8 * l + 2 * e] = u2f(w << 16);
+            xv[i][8 * l + 2 * e + 1] = u2f(w & 0xFFFF0000u);
+          } else {
+            xv[i][4 * l + e] = u2f(w);
+          }
+        }
+    // Tensor scale (NVFP4 video transcript: one FP32 scale for the global
+    // range): s = amax / (6 * 448), 1 for an all-zero X, at least FLT_MIN; or
+    // the caller's.  Each workgroup reduces the whole of X itself.
+    if (flags & 1u) {
+      s_x = *tsA;
     } else {
-      if (c < KT * 256u) *reinterpret_cast<v4i*>(lds_a + 16u * c) = ald[i];
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < XNB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(xv[i][e]));
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if (lane == 0) red[0][0][wave] = m;
+      __syncthreads();
+      float amax = 0.0f;
+#pragma unroll
+      for (int w = 0; w < (int)GV_WAVES; ++w) amax = fmaxf(amax, red[0][0][w]);
+      if (amax > 0.0f) {
+        s_x = amax / 2688.0f;
+        if (s_x < FLT_MIN) s_x = FLT_MIN;
+      }
+      if (blockIdx.x == 0 && tid == 0 && ts_out) *ts_out = s_x;
+    }
+    // Quantise each block exactly as the quantiser does and stage the
+    // dequantised values E2M1 * E4M3 (exact in FP16; s_x waits for the end).
+#pragma unroll
+    for (int i = 0; i < XNB; ++i) {
+      const uint32_t b = tid + 1024u * i;
+      const uint32_t row = b / xbpr, bk = b % xbpr;
+      if (row < M) {
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(xv[i][e]));
+        const uint32_t sb = e4m3_encode((am / 6.0f) / s_x);
+        float y[16];
+        if (sb == 0u) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) y[e] = __builtin_copysignf(0.0f, xv[i][e]);   // x / inf
+        } else {
+          const float d = e4m3_value(sb) * s_x;
+          const float rd = 1.0f / d;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) y[e] = nv_div(xv[i][e], d, rd);
+        }
+        const v2h sp = scale_pair(sb);
+        uint8_t* dst = lds_a + row * RS + 32u * bk;
+        *reinterpret_cast<v8h*>(dst) = decode8(pack8(y), sp);
+        *reinterpret_cast<v8h*>(dst + 16u) = decode8(pack8(y + 8), sp);
+      }
     }
   }
-  if (AMODE == kACode && tid < KT * 32u) *reinterpret_cast<v4i*>(lds_a + KT * 4096u + 16u * tid) = ascl;
-  if (AMODE == kAF16 && tid < 32u) *reinterpret_cast<v4i*>(lds_a + zero_off + 16u * tid) = v4i{};
+  if (AMODE != kACode && tid < 32u) *reinterpret_cast<v4i*>(lds_a + zero_off + 16u * tid) = v4i{};
   __syncthreads();
 
   // ---- main loop
-  const float scale = *tsA * *tsW;
+  const float scale = (AMODE == kFused ? s_x : *tsA) * *tsW;
   // AF16: lanes of rows >= M read a 512-byte zero block at a fixed place.
   const uint32_t a_row_off = li * RS + 64u * lj;
   v16f acc0 = v16f{}, acc1 = v16f{};
-  for (uint32_t jj = 0; jj < T; jj += GV_PD) {
+  for (uint32_t jj = 0; jj < T; jj += PD) {
 #pragma unroll
-    for (int p = 0; p < (int)GV_PD; ++p) {
+    for (int p = 0; p < PD; ++p) {
       const uint32_t j = jj + p;
       if (j >= T) break;
       const uint32_t kt = wave + GV_WAVES * (j % NJ);
@@ -192,7 +298,7 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
           for (int g = 0; g < 4; ++g) {
             const v8h b = decode8((uint32_t)d.w[s2][g], g < 2 ? w0 : w1);
             v8h a;
-            if (AMODE == kAF16)
+            if (AMODE != kACode)
               a = *reinterpret_cast<const v8h*>(lds_a + abase + s2 * 128u + 16u * g);
             else
               a = decode8((uint32_t)acodes[g], g < 2 ? a0 : a1);
@@ -203,7 +309,7 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
           }
         }
       }
-      if (j + GV_PD < T) issue(ring[p], j + GV_PD);
+      if (j + PD < T) issue(ring[p], j + PD);
 
       if (j % NJ == NJ - 1u) {
         // End of a row block: waves 0..3 gather waves 4..15 (in order of w),
@@ -271,27 +377,66 @@ static int gemv_amode(int64_t M, int64_t K) {
   return -1;
 }
 
+// The fused path stages X as FP16 (as kAF16) and holds XNB blocks per thread.
+static bool gemv_fused_fits(int64_t M, int64_t K, int x_dtype) {
+  const int64_t KT = (K + 255) / 256, Kp = KT * 256;
+  const int64_t nb = x_dtype == kDtBF16 ? GV_X_BLOCKS_BF16 : GV_X_BLOCKS_F32;
+  return M * (2 * Kp + 16) + 512 <= (int64_t)GV_A_BYTES && M * (Kp / 16) <= 1024 * nb;
+}
+
 }  // namespace
 
 bool gemv_nv_applies(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 32 && N >= 1 && gemv_amode(M, K) >= 0;
 }
 
+bool gemv_nv_fused_applies(int64_t M, int64_t N, int64_t K, int x_dtype) {
+  return M >= 1 && M <= 32 && N >= 1 && gemv_fused_fits(M, K, x_dtype);
+}
+
+static dim3 gemv_grid(int64_t N) {
+  const uint32_t nblocks = (uint32_t)((N + 31) / 32);
+  return dim3(nblocks < 256u ? nblocks : 256u);
+}
+
 hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                           int out_dtype, hipStream_t stream) {
-  const uint32_t nblocks = (uint32_t)((N + 31) / 32);
-  const dim3 grid(nblocks < 256u ? nblocks : 256u);
-  const dim3 block(GV_WAVES * 64);
+  const dim3 grid = gemv_grid(N), block(GV_WAVES * 64);
   const uint32_t m = (uint32_t)M, n = (uint32_t)N, k = (uint32_t)K;
   const int mode = gemv_amode(M, K);
+#define GV_LAUNCH(MODE, OUTT) \
+  gemv_nv_kernel<MODE, OUTT, kDtBF16, 1><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k, nullptr, \
+                                                                     nullptr, 0u)
   if (mode == kAF16) {
-    if (out_dtype == 0) gemv_nv_kernel<kAF16, 0><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
-    else gemv_nv_kernel<kAF16, 1><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+    if (out_dtype == 0) GV_LAUNCH(kAF16, 0);
+    else GV_LAUNCH(kAF16, 1);
   } else {
-    if (out_dtype == 0) gemv_nv_kernel<kACode, 0><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
-    else gemv_nv_kernel<kACode, 1><<<grid, block, 0, stream>>>(A, sA, B, sB, tsA, tsB, C, m, n, k);
+    if (out_dtype == 0) GV_LAUNCH(kACode, 0);
+    else GV_LAUNCH(kACode, 1);
   }
+#undef GV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_nv_fused(const void* X, int x_dtype, float* x_tensor_scale, unsigned flags,
+                                const uint8_t* B, const uint8_t* sB, const float* tsB, void* C, int64_t M,
+                                int64_t N, int64_t K, int out_dtype, hipStream_t stream) {
+  const dim3 grid = gemv_grid(N), block(GV_WAVES * 64);
+  const uint32_t m = (uint32_t)M, n = (uint32_t)N, k = (uint32_t)K;
+  const float* ts_in = x_tensor_scale;
+  float* ts_out = (flags & 1u) ? nullptr : x_tensor_scale;
+#define GV_LAUNCH(OUTT, XT)                                                                                      \
+  gemv_nv_kernel<kFused, OUTT, XT, GV_FUSED_PD><<<grid, block, 0, stream>>>(nullptr, nullptr, B, sB, ts_in, tsB, C, \
+                                                                              m, n, k, X, ts_out, flags)
+  if (x_dtype == kDtBF16) {
+    if (out_dtype == 0) GV_LAUNCH(0, kDtBF16);
+    else GV_LAUNCH(1, kDtBF16);
+  } else {
+    if (out_dtype == 0) GV_LAUNCH(0, kDtF32);
+    else GV_LAUNCH(1, kDtF32);
+  }
+#undef GV_LAUNCH
   return hipGetLastError();
 }
 

@@ -22,7 +22,6 @@ namespace fp4 {
 
 namespace {
 
-constexpr int kDtF32 = 0, kDtBF16 = 1;
 
 template <int DT>
 __device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
@@ -44,19 +43,6 @@ __device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
       v[2 * k + 1] = u2f(a[k] & 0xFFFF0000u);
     }
   }
-}
-
-// Pack 8 already-scaled values into 8 E2M1 codes (element 2i in the low nibble
-// of byte i).  The gfx950 converter rounds x/1.0 to the nearest E2M1 value,
-// ties to even, saturating at +-6, and keeps the sign (so -0 and negative values
-// that round to zero give code 8).
-__device__ __forceinline__ uint32_t pack8(const float y[8]) {
-  uint32_t r = 0;
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], 1.0f, 0);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], 1.0f, 1);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], 1.0f, 2);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], 1.0f, 3);
-  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -193,10 +179,16 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
   const float r = (am / 6.0f) / s_t;
   const uint32_t sb = e4m3_encode(r);
   if (valid) {
-    const float d = (sb == 0u) ? __builtin_inff() : e4m3_value(sb) * s_t;
     float y[8];
+    if (sb == 0u) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = v[k] / d;
+      for (int k = 0; k < 8; ++k) y[k] = __builtin_copysignf(0.0f, v[k]);   // x / inf
+    } else {
+      const float d = e4m3_value(sb) * s_t;
+      const float rd = 1.0f / d;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = nv_div(v[k], d, rd);
+    }
     *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
   }
   // Tile T = lane / 32 holds blocks q = 0..15 of 16 values (block q in lanes

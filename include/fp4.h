@@ -176,6 +176,30 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
                      const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N, int64_t K,
                      int fmt, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode-shape NVFP4 GEMM with the activation quantised inside the call (one
+ * kernel): C[M x N] = (X^ . W^T) * s_x * tsW, where X^, s_x are what
+ * fp4_quantize(X, FP4_NVFP4, ...) would produce -- the tensor scale from X's
+ * largest magnitude (s_x = amax / 2688, 1 for an all-zero X, at least FLT_MIN)
+ * unless flags has FP4_TS_GIVEN, 16-value blocks with E4M3 scales, E2M1 codes
+ * -- and W^ the NVFP4 weights (codes, scales, tensor scale tsW).  Same
+ * arithmetic as fp4_quantize followed by fp4_gemm ("Rubin FP4 GEMM deep dive"
+ * §1.2, §6.2: decoding moves every weight once per token, so the activation
+ * work is folded into the weight stream); the quantised X is not stored.
+ *   X: M x K, FP32 or BF16 (x_dtype), K contiguous, 16-byte aligned.
+ *   x_tensor_scale: with FP4_TS_GIVEN, the given s_x (device FP32, required);
+ *   otherwise, if non-NULL, receives the computed s_x.
+ *   W, sW, tsW: as B, sB, tsB of fp4_gemm.  C: M x N, FP32 or BF16.
+ * Applies to small activations (each workgroup stages all of X: for example
+ * M <= 8 with K = 8192 and BF16 X); fp4_gemm_nvfp4_act_supported says whether
+ * a shape is; otherwise FP4_ERR_SHAPE (use fp4_quantize + fp4_gemm).
+ * Requirements: K % 32 == 0.  M == 0 or N == 0 is a no-op. */
+int fp4_gemm_nvfp4_act(const void* X, int x_dtype, float* x_tensor_scale, unsigned flags, const uint8_t* W,
+                       const uint8_t* sW, const float* tsW, void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                       void* stream);
+
+/* 1 if fp4_gemm_nvfp4_act takes this shape and X dtype, else 0.  Host-only. */
+int fp4_gemm_nvfp4_act_supported(int64_t M, int64_t N, int64_t K, int x_dtype);
+
 /* Static string naming a status code. */
 const char* fp4_status_string(int status);
 

@@ -140,3 +140,40 @@ def test_grouped_argument_errors(L):
     assert call(total=0) == 0
     assert call(row_idx=None) == -1
     assert call(off=FAKE + 2) == -3
+
+
+def test_fused_decode_argument_errors(L):
+    g = fp4.fp4_gemm_nvfp4_act
+
+    def call(**kw):
+        a = dict(X=FAKE, xdt=1, ts=None, flags=0, W=FAKE, sW=FAKE, tsW=FAKE, C=FAKE, M=1, N=64, K=8192, out=1)
+        a.update(kw)
+        return g(a["X"], a["xdt"], a["ts"], a["flags"], a["W"], a["sW"], a["tsW"], a["C"], a["M"], a["N"], a["K"],
+                 a["out"], None)
+
+    assert call(xdt=2) == -5
+    assert call(out=3) == -5
+    assert call(flags=2) == -8
+    assert call(K=8176) == -2          # K % 32
+    assert call(M=-1) == -2
+    assert call(M=16) == -2            # 16 x 8192 does not fit the fused staging
+    assert call(M=0, C=None) == 0      # empty output: no-op
+    assert call(C=None) == -1
+    assert call(tsW=None) == -1
+    assert call(X=None) == -1
+    assert call(flags=1) == -1         # a given tensor scale must be passed
+    assert call(X=ODD) == -3
+    assert call(C=FAKE + 1, out=1) == -3
+
+
+def test_fused_decode_supported_shapes(L):
+    s = fp4.fp4_gemm_nvfp4_act_supported
+    assert s(1, 8192, 8192, fp4.BF16) == 1
+    assert s(8, 8192, 8192, fp4.BF16) == 1
+    assert s(16, 8192, 8192, fp4.BF16) == 0
+    assert s(4, 8192, 8192, fp4.F32) == 1
+    assert s(8, 8192, 8192, fp4.F32) == 0
+    assert s(32, 64, 1024, fp4.BF16) == 1
+    assert s(33, 64, 1024, fp4.BF16) == 0
+    assert s(1, 64, 48, fp4.BF16) == 0  # K % 32
+    assert s(0, 64, 1024, fp4.BF16) == 0

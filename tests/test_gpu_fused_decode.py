@@ -1,0 +1,110 @@
+"""The decode GEMM with the activation quantised inside the call
+(fp4_gemm_nvfp4_act) against the oracle: the oracle quantises X to NVFP4 (its
+own tensor scale, or the given one) and multiplies in FP64; every output
+element must lie within 1e-5 * sum|ab| (FP32) or inside the BF16-rounded
+interval.  The computed tensor scale must equal the oracle's bit for bit, and
+the result must equal fp4_quantize + fp4_gemm bit for bit (same staged values,
+same summation order)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import assert_gemm_close, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(orc, M, N, K, x, w, out_bf16, given_ts=None):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    say("fused decode M=%d N=%d K=%d x=%s bf16=%s ts=%s" % (M, N, K, x.dtype, out_bf16, given_ts))
+    qw = fp4.quantize(to_dev(w), fp4.NVFP4)
+    xd = to_dev(x)
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    ts_out = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    ts_in = None if given_ts is None else torch.tensor([given_ts], dtype=torch.float32, device="cuda")
+    C = fp4.gemm_nvfp4_act(xd, qw, tensor_scale=ts_in, ts_out=ts_out, out_dtype=odt)
+    rx = orc.quantize(x, orc.FMT_NVFP4, tensor_scale=given_ts)
+    rw = orc.quantize(w, orc.FMT_NVFP4)
+    if given_ts is None:
+        assert to_host(ts_out)[0] == np.float32(rx[3])
+    else:
+        assert to_host(ts_out)[0] == -1.0          # untouched when the scale is given
+    Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, N, K, orc.FMT_NVFP4, tsA=rx[3], tsB=rw[3])
+    assert_gemm_close(orc, to_host(C), Cref, T, out_bf16, "fused M=%d N=%d K=%d" % (M, N, K))
+    # Same bits as the two-call path.
+    qx = fp4.quantize(xd, fp4.NVFP4, tensor_scale=ts_in)
+    C2 = fp4.gemm(qx, qw, out_dtype=odt)
+    assert torch.equal(C.view(torch.uint8), C2.view(torch.uint8))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (2, 64, 288), (4, 257, 8192),
+                                   (32, 70, 1024)])
+@pytest.mark.parametrize("bf16_x", [True, False])
+def test_fused_decode_matches_oracle(orc, M, N, K, bf16_x):
+    x = synth.gaussian(300 + M, (M, K), every=97)
+    if bf16_x:
+        x = synth.to_bf16_bits(x)
+    w = synth.gaussian(400 + N, (N, K), std=0.02, bernoulli=0.001)
+    _case(orc, M, N, K, x, w, out_bf16=(M % 2 == 1))
+
+
+def test_fused_decode_given_tensor_scale(orc):
+    M, N, K = 4, 200, 1024
+    x = synth.to_bf16_bits(synth.gaussian(311, (M, K)))
+    w = synth.gaussian(411, (N, K), std=0.02)
+    _case(orc, M, N, K, x, w, out_bf16=True, given_ts=0.0017)
+
+
+def test_fused_decode_edge_values(orc):
+    """Rows of zeros, -0, tiny blocks (subnormal and zero E4M3 scales) next to
+    large ones, values on E2M1 rounding ties."""
+    M, N, K = 6, 128, 512
+    x = synth.gaussian(321, (M, K))
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :256] *= 1e-6                 # blocks far below the tensor maximum
+    x[3] = np.tile(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32), K // 8)
+    x[3, ::16] = 6.0                    # block max 6 with s_t such that d = 1 where possible
+    x[4, 1:] = 0.0
+    x[4, 0] = 3e-30                    # a single tiny value: tensor scale near FLT_MIN territory
+    w = synth.gaussian(421, (N, K), std=0.02)
+    _case(orc, M, N, K, x.astype(np.float32), w, out_bf16=False)
+
+
+def test_fused_decode_all_zero_x(orc):
+    M, N, K = 3, 96, 256
+    _case(orc, M, N, K, np.zeros((M, K), np.float32), synth.gaussian(431, (N, K)), out_bf16=False)
+
+
+def test_fused_decode_many_row_blocks(orc):
+    """More 32-row weight blocks than the grid holds (grid-stride loop)."""
+    M, N, K = 2, 256 * 32 + 48, 256
+    x = synth.to_bf16_bits(synth.gaussian(341, (M, K)))
+    w = synth.gaussian(441, (N, K), std=0.02)
+    _case(orc, M, N, K, x, w, out_bf16=True)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_fused_decode_8192_sampled(orc, M):
+    """The decode workload (W 8192 x 8192 NVFP4, X M x 8192 BF16): all rows x
+    64 sampled columns against the oracle, and the same bits as the two-call
+    path everywhere."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    w = synth.nvfp4_decode_weight()
+    x = synth.nvfp4_decode_act(M)
+    say("fused decode 8192 M=%d" % M)
+    qw = fp4.quantize(to_dev(w), fp4.NVFP4)
+    xd = to_dev(x)
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    C = fp4.gemm_nvfp4_act(xd, qw, ts_out=ts, out_dtype=torch.bfloat16)
+    qx = fp4.quantize(xd, fp4.NVFP4)
+    C2 = fp4.gemm(qx, qw, out_dtype=torch.bfloat16)
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    rx = orc.quantize(x, orc.FMT_NVFP4)
+    assert to_host(ts)[0] == np.float32(rx[3])
+    cols = np.random.default_rng(M).choice(8192, 64, replace=False)
+    rw = orc.quantize(w[cols], orc.FMT_NVFP4, tensor_scale=float(to_host(qw.tensor_scale)[0]))
+    Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, 64, 8192, orc.FMT_NVFP4, tsA=rx[3], tsB=rw[3])
+    assert_gemm_close(orc, to_host(C)[:, cols], Cref, T, True, "fused decode 8192 M=%d" % M)

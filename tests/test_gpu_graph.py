@@ -72,6 +72,33 @@ def test_graph_nvfp4_decode(orc, M):
     _replay_and_check(g, C, ref, lambda: fp4.gemm(fp4.quantize(other, fp4.NVFP4), qw))
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_graph_nvfp4_fused_decode(orc, M):
+    """The one-kernel decode step (activation quantised inside) under graph
+    replay; its result equals the two-call path's bits."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    N, K = 1024, 2048
+    w = synth.gaussian(3, (N, K), std=0.02, bernoulli=0.001)
+    x = synth.to_bf16_bits(synth.gaussian(203 + M, (M, K)))
+    say("graph fused decode M=%d N=%d K=%d" % (M, N, K))
+    qw = fp4.quantize(to_dev(w), fp4.NVFP4)
+    xd = to_dev(x)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        fp4.gemm_nvfp4_act(xd, qw, out=C)
+
+    step()
+    torch.cuda.synchronize()
+    ref = C.clone()
+    C2 = fp4.gemm(fp4.quantize(xd, fp4.NVFP4), qw, out_dtype=torch.bfloat16)
+    assert torch.equal(ref.view(torch.int16), C2.view(torch.int16))
+    g = _capture(step, 3)
+    other = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    _replay_and_check(g, C, ref, lambda: fp4.gemm_nvfp4_act(other, qw))
+
+
 def test_graph_mxfp4_small(orc):
     import block_scaled_fp4_03_amd as fp4
     import torch
