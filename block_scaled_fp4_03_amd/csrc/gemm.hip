@@ -88,16 +88,22 @@ __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u
 template <int SUB>
 __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u32x2 (&sa)[4],
                                         const u32x2 (&sb)[2]) {
+  // Scale bytes 2 SUB, 2 SUB + 1 of the lane's 8 (groups 0-1, 2-3) as FP16,
+  // two per conversion.
+  v2h spa[4], spb[2];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    spa[r] = (SUB & 1) ? e4m3x2_to_f16<true>(sa[r][SUB >> 1]) : e4m3x2_to_f16<false>(sa[r][SUB >> 1]);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    spb[c] = (SUB & 1) ? e4m3x2_to_f16<true>(sb[c][SUB >> 1]) : e4m3x2_to_f16<false>(sb[c][SUB >> 1]);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int byte = 2 * SUB + (g >> 1);  // scale byte of this group within the lane's 8 bytes
     v8h a[4], b[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      a[r] = decode8((uint32_t)o.a[r][g], scale_pair((sa[r][byte >> 2] >> (8 * (byte & 3))) & 0xFFu));
+    for (int r = 0; r < 4; ++r) a[r] = decode8((uint32_t)o.a[r][g], g < 2 ? splat_lo(spa[r]) : splat_hi(spa[r]));
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      b[c] = decode8((uint32_t)o.b[c][g], scale_pair((sb[c][byte >> 2] >> (8 * (byte & 3))) & 0xFFu));
+    for (int c = 0; c < 2; ++c) b[c] = decode8((uint32_t)o.b[c][g], g < 2 ? splat_lo(spb[c]) : splat_hi(spb[c]));
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
