@@ -111,16 +111,17 @@ __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u
   }
 }
 
-// One LDS read of the next sub-step's operands after each MFMA (MXFP4).
-template <int FMT>
+// One LDS read of the next operands after each MFMA (MXFP4): NR of them
+// among the sub-step's 8 MFMAs.
+template <int FMT, int NR = 6>
 __device__ __forceinline__ void interleave_mfma_reads() {
   if (FMT == kFmtMX) {
 #pragma unroll
-    for (int k = 0; k < 6; ++k) {
+    for (int k = 0; k < NR; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (NR < 8) __builtin_amdgcn_sched_group_barrier(0x008, 8 - NR, 0);
   }
 }
 
@@ -357,16 +358,26 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      dma(k + 2u);
-      read_ops(k + 1u, 0, o0);
-      read_scales(k + 1u, sa_n, sb_n);
-      mma_sub<3>(acc, o1, sa, sb);
-      if (FMT == kFmtMX) {
-#pragma unroll
-        for (int k2 = 0; k2 < 8; ++k2) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+      // Waves w and w + 4 share a SIMD.  Dense MXFP4: waves 0-3 issue their
+      // copies of stage k+2 first and waves 4-7 after their sub-step 3 MFMAs,
+      // so that on every SIMD one wave keeps the matrix core busy while the
+      // other feeds the address unit (all eight issuing at once after the
+      // barrier left the matrix core idle for much of the copy issue).  The
+      // NVFP4 and grouped kernels keep one order: two copies of their
+      // sub-step code exceed the register budget.
+      constexpr bool STAGGER = FMT == kFmtMX && !GROUPED;
+      if (!STAGGER || wave < 4u) {
+        dma(k + 2u);
+        read_ops(k + 1u, 0, o0);
+        read_scales(k + 1u, sa_n, sb_n);
+        mma_sub<3>(acc, o1, sa, sb);
+        interleave_mfma_reads<FMT, 8>();
+      } else {
+        read_ops(k + 1u, 0, o0);
+        read_scales(k + 1u, sa_n, sb_n);
+        mma_sub<3>(acc, o1, sa, sb);
+        interleave_mfma_reads<FMT, 8>();
+        dma(k + 2u);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sa[r] = sa_n[r];
