@@ -34,6 +34,8 @@
 // every workgroup derives its (expert, m-tile, n-tile) from the device-side
 // group offsets (no host round trip), gathers its A rows through row_idx
 // (codes per lane, scale dwords per lane) and multiplies by that expert's B.
+#include <atomic>
+
 #include "fp4_launch.h"
 #include "gemm_common.h"
 
@@ -170,7 +172,23 @@ __device__ __forceinline__ uint32_t grouped_total_tiles(const Groups& gp, uint32
   return total;
 }
 
-template <int FMT, int OUT, bool GROUPED>
+// Operand addressing of one output tile: scalar bases and byte ranges, plus
+// the per-lane source offsets of A (gathered rows when grouped).
+struct TileAddr {
+  const uint8_t* a_base;
+  const uint8_t* sa_base;
+  const uint8_t* b_tile;
+  const uint8_t* sb_tile;
+  uint32_t a_bytes, sa_bytes, b_bytes, sb_bytes;
+  uint32_t m0, n0, rowsA, row0;
+  uint32_t voffA[4];
+  uint32_t svoffA;
+};
+
+// PERSIST: workgroups walk tiles (grid <= resident workgroups) with the next
+// tile's first stages copied during this one's last iterations, and store C
+// from registers; else one tile per workgroup, C stored through LDS.
+template <int FMT, int OUT, bool GROUPED, bool PERSIST>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
                                                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB,
                                                      const float* __restrict__ tsA, const float* __restrict__ tsB,
@@ -189,33 +207,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const uint32_t wm = wave >> 2, wn = wave & 3u;  // 2 x 4 waves, 128 x 64 each
 
-  // ---- which tile: rows [row0 + m0, +rowsA) of A / C, columns [n0, +rowsB)
-  uint32_t m0, n0, rowsA, row0 = 0, expert = 0;
+  // ---- tile schedule.  Workgroup b takes the virtual tiles v = b, b + G, ...
+  // (G = grid size, a multiple of 8, so that v % 8 and with it the XCD stay
+  // fixed).  Dense: v -> tile as tile_coords.  Grouped: tiles of the expert
+  // list, v -> t = (v % 8) * ceil(total / 8) + v / 8.
+  uint32_t total, per_xcd = 0;
   if (GROUPED) {
-    const uint32_t total = grouped_total_tiles(gp, tilesN);
-    const uint32_t per_xcd = (total + 7u) / 8u;
-    const uint32_t t = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
-    if ((blockIdx.x >> 3) >= per_xcd || t >= total) return;
-    uint32_t cnt, tm, tn;
-    grouped_tile(gp, t, tilesN, expert, row0, cnt, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
-    rowsA = (cnt - m0) < BM ? (cnt - m0) : BM;
-    B += (size_t)expert * gp.b_codes_stride;
-    sB += (size_t)expert * gp.b_scales_stride;
+    total = grouped_total_tiles(gp, tilesN);
+    per_xcd = (total + 7u) / 8u;
   } else {
-    uint32_t tm, tn;
-    tile_coords(blockIdx.x, tilesM, tilesN, GROUP_M, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
-    rowsA = (M - m0) < BM ? (M - m0) : BM;
+    total = tilesM * tilesN;
   }
-  const uint32_t rowsB = (N - n0) < BN ? (N - n0) : BN;
-  const uint8_t* const b_tile = B + (size_t)n0 * ldb;
-  const uint32_t b_bytes = rowsB * ldb;
-  const uint32_t RTB = (N + 31u) / 32u;
-  const uint8_t* const sb_tile = sB + (size_t)(n0 / 32u) * srow;
-  const uint32_t sb_bytes = (RTB > n0 / 32u ? RTB - n0 / 32u : 0u) * srow;
+  auto tile_of = [&](uint32_t v, uint32_t& t) -> bool {
+    if (GROUPED) {
+      t = (v & 7u) * per_xcd + (v >> 3);
+      return (v >> 3) < per_xcd && t < total;
+    }
+    t = v;
+    return v < total;
+  };
 
   // ---- direct-to-LDS load plan.  One code load (1 KB) fills 8 rows: lane L
   // fills LDS row L/8, position L%8, i.e. fetches the row's chunk
@@ -223,59 +233,88 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   // of B and scale tile w of A and of B.
   const uint32_t grow = lane >> 3;
   const uint32_t gchunk = (lane & 7u) ^ ((4u * (wave & 1u) + (lane >> 4)) & 7u);
-  uint32_t voffA[4], voffB[4];
-  uint32_t svoffA;  // A scale source offset (per lane when grouped)
+  uint32_t voffB[4];
   const uint32_t svoffB = (wave * KT) * STILE + lane * 4u;
-  const uint8_t* a_base;
-  uint32_t a_bytes, sa_bytes;
-  const uint8_t* sa_base;
 #pragma unroll
   for (int q = 0; q < 4; ++q) voffB[q] = (8u * (wave + 8u * q) + grow) * ldb + 16u * gchunk;
-  if (GROUPED) {
-    // Gathered rows: lane offsets from the A row of each tile row; rows past
-    // the group get an out-of-range offset and load zeros.
-    a_base = A;
-    a_bytes = gp.A_rows * ldb;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t r = 8u * (wave + 8u * q) + grow;
-      voffA[q] = r < rowsA ? (uint32_t)gp.row_idx[row0 + m0 + r] * ldb + 16u * gchunk : 0x80000000u;
-    }
-    // Scale dwords: lane L = 32j + i of scale block `wave` is row i, chunk
-    // parity j, found at the gathered row's own scale tile.
-    const uint32_t i = lane & 31u, r = 32u * wave + i;
-    if (r < rowsA) {
-      const uint32_t tok = (uint32_t)gp.row_idx[row0 + m0 + r];
-      svoffA = (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u;
-    } else {
-      svoffA = 0x80000000u;
-    }
-    sa_base = sA;
-    sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
-  } else {
-    a_base = A + (size_t)m0 * ldb;
-    a_bytes = rowsA * ldb;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) voffA[q] = voffB[q];
-    const uint32_t RTA = (M + 31u) / 32u;
-    sa_base = sA + (size_t)(m0 / 32u) * srow;
-    sa_bytes = (RTA > m0 / 32u ? RTA - m0 / 32u : 0u) * srow;
-    svoffA = svoffB;
-  }
 
-  auto dma = [&](uint32_t stage_k) {
+  auto make_tile = [&](uint32_t t, TileAddr& T) {
+    uint32_t rowsA, row0 = 0, expert = 0, m0, n0;
+    const uint8_t* Bx = B;
+    const uint8_t* sBx = sB;
+    if (GROUPED) {
+      uint32_t cnt, tm, tn;
+      grouped_tile(gp, t, tilesN, expert, row0, cnt, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rowsA = (cnt - m0) < BM ? (cnt - m0) : BM;
+      Bx += (size_t)expert * gp.b_codes_stride;
+      sBx += (size_t)expert * gp.b_scales_stride;
+    } else {
+      uint32_t tm, tn;
+      tile_coords(t, tilesM, tilesN, GROUP_M, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rowsA = (M - m0) < BM ? (M - m0) : BM;
+    }
+    T.m0 = m0;
+    T.n0 = n0;
+    T.rowsA = rowsA;
+    T.row0 = row0;
+    const uint32_t rowsB = (N - n0) < BN ? (N - n0) : BN;
+    T.b_tile = Bx + (size_t)n0 * ldb;
+    T.b_bytes = rowsB * ldb;
+    const uint32_t RTB = (N + 31u) / 32u;
+    T.sb_tile = sBx + (size_t)(n0 / 32u) * srow;
+    T.sb_bytes = (RTB > n0 / 32u ? RTB - n0 / 32u : 0u) * srow;
+    if (GROUPED) {
+      // Gathered rows: lane offsets from the A row of each tile row; rows past
+      // the group get an out-of-range offset and load zeros.
+      T.a_base = A;
+      T.a_bytes = gp.A_rows * ldb;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t r = 8u * (wave + 8u * q) + grow;
+        T.voffA[q] = r < rowsA ? (uint32_t)gp.row_idx[row0 + m0 + r] * ldb + 16u * gchunk : 0x80000000u;
+      }
+      // Scale dwords: lane L = 32j + i of scale block `wave` is row i, chunk
+      // parity j, found at the gathered row's own scale tile.
+      const uint32_t i = lane & 31u, r = 32u * wave + i;
+      if (r < rowsA) {
+        const uint32_t tok = (uint32_t)gp.row_idx[row0 + m0 + r];
+        T.svoffA = (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u;
+      } else {
+        T.svoffA = 0x80000000u;
+      }
+      T.sa_base = sA;
+      T.sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
+    } else {
+      // Dense tiles read A with B's per-lane offsets (voffA unused).
+      T.a_base = A + (size_t)m0 * ldb;
+      T.a_bytes = rowsA * ldb;
+      const uint32_t RTA = (M + 31u) / 32u;
+      T.sa_base = sA + (size_t)(m0 / 32u) * srow;
+      T.sa_bytes = (RTA > m0 / 32u ? RTA - m0 / 32u : 0u) * srow;
+    }
+  };
+
+  // Copy stage `stage_k` of tile T into LDS buffer `buf`; stages past K (or
+  // live == false) read out of range: zero fill, no memory traffic, and the
+  // same instruction count, so that the wait counts stay exact.
+  auto dma = [&](const TileAddr& T, uint32_t stage_k, uint32_t buf, bool live) {
     // Stage offsets are folded into the descriptors (scalar registers), so
     // the per-lane offsets stay loop-invariant.
-    const uint32_t kb = opaque(stage_k * ROW_BYTES);
-    const uint32_t ko = opaque(stage_k * STILE);
-    uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + kb, uniform_rem(a_bytes, kb));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + kb, uniform_rem(b_bytes, kb));
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa_base + ko, uniform_rem(sa_bytes, ko));
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sb_tile + ko, uniform_rem(sb_bytes, ko));
+    const uint32_t kb = opaque(live ? stage_k * ROW_BYTES : 0xFFFFFFFFu);
+    const uint32_t ko = opaque(live ? stage_k * STILE : 0xFFFFFFFFu);
+    uint8_t* st = lds + buf * STAGE_BYTES;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(T.a_base + (live ? kb : 0u), uniform_rem(T.a_bytes, kb));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(T.b_tile + (live ? kb : 0u), uniform_rem(T.b_bytes, kb));
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(T.sa_base + (live ? ko : 0u), uniform_rem(T.sa_bytes, ko));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(T.sb_tile + (live ? ko : 0u), uniform_rem(T.sb_bytes, ko));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + 1024u * (wave + 8u * q)), 16, voffA[q], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + 1024u * (wave + 8u * q)), 16,
+                                               GROUPED ? T.voffA[q] : voffB[q], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + REGION + 1024u * (wave + 8u * q)), 16, voffB[q], 0,
                                                0, 0);
     }
@@ -284,7 +323,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       // NVFP4 lanes own 8 bytes: the two halves of a 512-byte tile are lanes
       // 0-31 and 32-63 of the dword copy.  (Grouped NVFP4 is not offered.)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + 2u * REGION + STILE * wave + 256u * h), 4,
-                                               svoffA + 256u * h, 0, 0, 0);
+                                               (GROUPED ? T.svoffA : svoffB) + 256u * h, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + 2u * REGION + SCALE_REGION + STILE * wave + 256u * h),
                                                4, svoffB + 256u * h, 0, 0, 0);
     }
@@ -300,15 +339,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   const uint32_t a_rows = 128u * (128u * wm);   // byte offset of this wave's first A row
   const uint32_t b_rows = 128u * (64u * wn);
 
-  auto read_ops = [&](uint32_t stage_k, int q, Ops& o) {
-    const uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES;
+  auto read_ops = [&](uint32_t buf, int q, Ops& o) {
+    const uint8_t* st = lds + buf * STAGE_BYTES;
 #pragma unroll
     for (int r = 0; r < 4; ++r) o.a[r] = *reinterpret_cast<const v4i*>(st + a_rows + 4096u * r + rd[q]);
 #pragma unroll
     for (int c = 0; c < 2; ++c) o.b[c] = *reinterpret_cast<const v4i*>(st + REGION + b_rows + 4096u * c + rd[q]);
   };
-  auto read_scales = [&](uint32_t stage_k, S (&sa)[4], S (&sb)[2]) {
-    const uint8_t* st = lds + (stage_k % NSTAGE) * STAGE_BYTES + 2u * REGION;
+  auto read_scales = [&](uint32_t buf, S (&sa)[4], S (&sb)[2]) {
+    const uint8_t* st = lds + buf * STAGE_BYTES + 2u * REGION;
     constexpr uint32_t LB = STILE / 64u;  // bytes per lane
 #pragma unroll
     for (int r = 0; r < 4; ++r) sa[r] = *reinterpret_cast<const S*>(st + STILE * (4u * wm + r) + LB * lane);
@@ -317,175 +356,258 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       sb[c] = *reinterpret_cast<const S*>(st + SCALE_REGION + STILE * (2u * wn + c) + LB * lane);
   };
 
-  v16f acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  uint32_t v = blockIdx.x, t;
+  if (!tile_of(v, t)) return;
+  TileAddr cur;
+  make_tile(t, cur);
+  const float scale = (tsA ? *tsA : 1.0f) * (tsB ? *tsB : 1.0f);
 
-  // Stage k covers K values [256k, 256k + 256) in four 64-value sub-steps.
+  // Stage k of a tile covers K values [256k, 256k + 256) in four 64-value
+  // sub-steps; stages alternate between the two LDS buffers in one sequence
+  // over all the workgroup's tiles (g = stage number in that sequence).
   // Sub-steps 0-2 each multiply while the next sub-step's operands are read
-  // from LDS; then wait for this wave's loads of stage k+1, barrier (all of
-  // stage k+1 has landed; every wave is done reading stage k), launch the
-  // loads of stage k+2 into stage k's buffer, read sub-step 0 of k+1 and its
-  // scales, and multiply sub-step 3.  A last, partial stage runs over codes
-  // past K; their scale bytes are the tile's padding (0), which makes those
-  // products zero (E8M0: 2^-127 on both operands, <= 36 * 2^-254, zero in
-  // FP32; E4M3: an FP16 zero), so they add nothing.
+  // from LDS; then wait for this wave's copies of stage g+1, barrier (stage
+  // g+1 has landed everywhere; every wave is done reading stage g), copy stage
+  // g+2 into stage g's buffer, read stage g+1's first operands and scales, and
+  // multiply sub-step 3.  Once a tile has no stages left to copy, its last two
+  // iterations copy the first two stages of the workgroup's next tile, so
+  // that tile starts without waiting while this one's results are stored.  A
+  // last, partial stage runs over codes past K; their scale bytes are the
+  // tile's padding (0), which makes those products zero (E8M0: 2^-127 on both
+  // operands, <= 36 * 2^-254, zero in FP32; E4M3: an FP16 zero).
+  Ops o0, o1;
+  S sa[4], sb[2], sa_n[4], sb_n[2];
   if (KT > 0) {
-    Ops o0, o1;
-    S sa[4], sb[2], sa_n[4], sb_n[2];
-    dma(0);
-    dma(1);
+    dma(cur, 0, 0, true);
+    dma(cur, 1, 1, KT > 1u);
     if (LOADS_PER_STAGE == 10)
       asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read_ops(0, 0, o0);
-    read_scales(0, sa, sb);
+  }
+  uint32_t g = 0;                                // sequence number of cur's stage 0
+  while (true) {
+    // The tile's first operands (its stage 0 landed at the last barrier).
+    read_ops(g & 1u, 0, o0);
+    read_scales(g & 1u, sa, sb);
+    uint32_t vn = v + gridDim.x, tn_;
+    // Tiles of one K stage leave no iteration to copy a next tile in: one
+    // tile per workgroup (the host sizes the grid accordingly).
+    const bool has_next = PERSIST && KT >= 2u && tile_of(vn, tn_);
+    TileAddr nxt = cur;
+    if (has_next) make_tile(tn_, nxt);
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
     for (uint32_t k = 0; k < KT; ++k) {
-      read_ops(k, 1, o1);
+      const uint32_t buf = (g + k) & 1u, nbuf = buf ^ 1u;
+      read_ops(buf, 1, o1);
       mma_sub<0>(acc, o0, sa, sb);
       interleave_mfma_reads<FMT>();
-      read_ops(k, 2, o0);
+      read_ops(buf, 2, o0);
       mma_sub<1>(acc, o1, sa, sb);
       interleave_mfma_reads<FMT>();
-      read_ops(k, 3, o1);
+      read_ops(buf, 3, o1);
       mma_sub<2>(acc, o0, sa, sb);
       interleave_mfma_reads<FMT>();
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // Stage g+k+2 goes into this buffer: this tile's stage k+2, or the next
+      // tile's stage k+2-KT.
+      const bool own = k + 2u < KT;
+      const TileAddr& src = own ? cur : nxt;
+      const uint32_t sk = own ? k + 2u : k + 2u - KT;
+      const bool live = own || has_next;
       // Waves w and w + 4 share a SIMD.  Dense MXFP4: waves 0-3 issue their
-      // copies of stage k+2 first and waves 4-7 after their sub-step 3 MFMAs,
-      // so that on every SIMD one wave keeps the matrix core busy while the
-      // other feeds the address unit (all eight issuing at once after the
-      // barrier left the matrix core idle for much of the copy issue).  The
-      // NVFP4 and grouped kernels keep one order: two copies of their
-      // sub-step code exceed the register budget.
+      // copies first and waves 4-7 after their sub-step 3 MFMAs, so that on
+      // every SIMD one wave keeps the matrix core busy while the other feeds
+      // the address unit (all eight issuing at once after the barrier left
+      // the matrix core idle for much of the copy issue).  The NVFP4 and
+      // grouped kernels keep one order: two copies of their sub-step code
+      // exceed the register budget.
       constexpr bool STAGGER = FMT == kFmtMX && !GROUPED;
       if (!STAGGER || wave < 4u) {
-        dma(k + 2u);
-        read_ops(k + 1u, 0, o0);
-        read_scales(k + 1u, sa_n, sb_n);
+        dma(src, sk, buf, live);
+        read_ops(nbuf, 0, o0);
+        read_scales(nbuf, sa_n, sb_n);
         mma_sub<3>(acc, o1, sa, sb);
         interleave_mfma_reads<FMT, 8>();
       } else {
-        read_ops(k + 1u, 0, o0);
-        read_scales(k + 1u, sa_n, sb_n);
+        read_ops(nbuf, 0, o0);
+        read_scales(nbuf, sa_n, sb_n);
         mma_sub<3>(acc, o1, sa, sb);
         interleave_mfma_reads<FMT, 8>();
-        dma(k + 2u);
+        dma(src, sk, buf, live);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sa[r] = sa_n[r];
 #pragma unroll
       for (int c = 0; c < 2; ++c) sb[c] = sb_n[c];
     }
-  }
 
-  // ---- epilogue: x tsA * tsB, FP32 or BF16 (round to nearest even).  Lane L
-  // of a 32x32 block holds column L%32, rows 8*(i/4) + 4*(L/32) + i%4.  The
-  // tile goes through LDS (free once every wave is past its last stage) so
-  // that global stores are 16-byte, row-contiguous; BF16 in one pass, FP32 in
-  // two passes of 128 rows.  A row pitch of C that is not a multiple of 16
-  // bytes, or an unaligned C, takes per-element stores.
-  const float scale = (tsA ? *tsA : 1.0f) * (tsB ? *tsB : 1.0f);
-  const size_t crow0 = (size_t)row0 + m0;
-  constexpr uint32_t EB = OUT == 0 ? 4u : 2u;              // bytes per element
-  constexpr uint32_t PASS_ROWS = OUT == 0 ? 128u : 256u;    // tile rows per pass
-  constexpr uint32_t LROW = BN * EB + 16u;                  // LDS row pitch (bank shift of 4 per row)
-  static_assert(PASS_ROWS * LROW <= NSTAGE * STAGE_BYTES, "epilogue tile must fit in LDS");
-  const bool vec_ok = ((N * EB) % 16u == 0u) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0u);
-  // No copy into LDS may still be in flight when LDS is reused or released
-  // (the last loop iterations copy zero-filled stages past K).
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (vec_ok) {
-    __syncthreads();
+    // ---- epilogue: x tsA * tsB, FP32 or BF16 (round to nearest even).  Lane
+    // L of a 32x32 block holds column L%32, rows 8*(i/4) + 4*(L/32) + i%4.
+    if constexpr (!PERSIST) {
+      // One tile per workgroup: the tile goes through LDS (free once every wave is
+      // past its last stage) so that global stores are 16-byte, row-contiguous;
+      // BF16 in one pass, FP32 in two passes of 128 rows.  A row pitch of C
+      // that is not a multiple of 16 bytes, or an unaligned C, takes
+      // per-element stores.
+      constexpr uint32_t EB = OUT == 0 ? 4u : 2u;              // bytes per element
+      constexpr uint32_t PASS_ROWS = OUT == 0 ? 128u : 256u;    // tile rows per pass
+      constexpr uint32_t LROW = BN * EB + 16u;                  // LDS row pitch (bank shift of 4 per row)
+      static_assert(PASS_ROWS * LROW <= NSTAGE * STAGE_BYTES, "epilogue tile must fit in LDS");
+      const bool vec_ok = ((N * EB) % 16u == 0u) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0u);
+      const size_t crow0 = (size_t)cur.row0 + cur.m0;
+      // The last iterations' zero-fill copies must have landed before LDS is
+      // reused.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (vec_ok) {
+        __syncthreads();
 #pragma unroll
-    for (uint32_t pass = 0; pass < 256u / PASS_ROWS; ++pass) {
-      if (PASS_ROWS == 256u || wm == pass) {
+        for (uint32_t pass = 0; pass < 256u / PASS_ROWS; ++pass) {
+          if (PASS_ROWS == 256u || wm == pass) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const uint32_t lcol = 64u * wn + 32u * c + li;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const uint32_t lrow =
+                      (PASS_ROWS == 256u ? 128u * wm : 0u) + 32u * r + 8u * (i >> 2) + 4u * lj + (i & 3);
+                  const float val = acc[r][c][i] * scale;
+                  if (OUT == 0)
+                    *reinterpret_cast<float*>(lds + lrow * LROW + 4u * lcol) = val;
+                  else
+                    *reinterpret_cast<uint16_t*>(lds + lrow * LROW + 2u * lcol) = f32_to_bf16(val);
+                }
+              }
+          }
+          __syncthreads();
+          // 16-byte chunks: BN * EB / 16 per row; 512 threads cover 512 chunks per step.
+          constexpr uint32_t CPR = BN * EB / 16u;
+          constexpr uint32_t STEPS = PASS_ROWS * CPR / 512u;
+#pragma unroll
+          for (uint32_t st = 0; st < STEPS; ++st) {
+            const uint32_t q = st * 512u + threadIdx.x;
+            const uint32_t lrow = q / CPR, ch = q % CPR;
+            const uint32_t row = pass * PASS_ROWS + lrow;
+            const uint32_t col = cur.n0 + ch * (16u / EB);
+            // N * EB is a multiple of 16 and col a multiple of 16 / EB, so a
+            // chunk that starts inside the row lies wholly inside it.
+            if (row < cur.rowsA && col < N)
+              *reinterpret_cast<v4i*>(static_cast<uint8_t*>(C) + ((crow0 + row) * N + col) * EB) =
+                  *reinterpret_cast<const v4i*>(lds + lrow * LROW + 16u * ch);
+          }
+          if (PASS_ROWS != 256u) __syncthreads();
+        }
+        break;
+      }
+    }
+    // Stores straight from registers (LDS may hold the next tile's first
+    // stages, or C's layout does not allow 16-byte stores).  One per-lane base per
+    // tile plus uniform row offsets (from an opaque N, so that they are not
+    // hoisted out of the tile loop into registers).
+    {
+      const uint32_t Nu = opaque(N);
+      const uint32_t lrow0 = 128u * wm + 4u * lj;                 // this lane's first row in the tile
+      const uint32_t lcol0 = cur.n0 + 64u * wn + li;              // this lane's first column
+      const size_t lbase = ((size_t)cur.row0 + cur.m0 + lrow0) * Nu + lcol0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t rr = 32u * r + 8u * (i >> 2) + (i & 3);  // row offset from lrow0
+          const size_t roff = (size_t)rr * Nu;
+          const bool row_ok = lrow0 + rr < cur.rowsA;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const uint32_t lcol = 64u * wn + 32u * c + li;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const uint32_t lrow = (PASS_ROWS == 256u ? 128u * wm : 0u) + 32u * r + 8u * (i >> 2) + 4u * lj + (i & 3);
-              const float v = acc[r][c][i] * scale;
+            if (row_ok && lcol0 + 32u * c < N) {
+              const float val = acc[r][c][i] * scale;
+              const size_t e = lbase + roff + 32u * c;
               if (OUT == 0)
-                *reinterpret_cast<float*>(lds + lrow * LROW + 4u * lcol) = v;
+                static_cast<float*>(C)[e] = val;
               else
-                *reinterpret_cast<uint16_t*>(lds + lrow * LROW + 2u * lcol) = f32_to_bf16(v);
+                static_cast<uint16_t*>(C)[e] = f32_to_bf16(val);
             }
           }
-      }
-      __syncthreads();
-      // 16-byte chunks: BN * EB / 16 per row; 512 threads cover 512 chunks per step.
-      constexpr uint32_t CPR = BN * EB / 16u;
-      constexpr uint32_t STEPS = PASS_ROWS * CPR / 512u;
-#pragma unroll
-      for (uint32_t st = 0; st < STEPS; ++st) {
-        const uint32_t q = st * 512u + threadIdx.x;
-        const uint32_t lrow = q / CPR, ch = q % CPR;
-        const uint32_t row = pass * PASS_ROWS + lrow;
-        const uint32_t col = n0 + ch * (16u / EB);
-        // N * EB is a multiple of 16 and col a multiple of 16 / EB, so a chunk
-        // that starts inside the row lies wholly inside it.
-        if (row < rowsA && col < N)
-          *reinterpret_cast<v4i*>(static_cast<uint8_t*>(C) + ((crow0 + row) * N + col) * EB) =
-              *reinterpret_cast<const v4i*>(lds + lrow * LROW + 16u * ch);
-      }
-      if (PASS_ROWS != 256u) __syncthreads();
-    }
-    return;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t col = n0 + 64u * wn + 32u * c + li;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t row = 128u * wm + 32u * r + 8u * (i >> 2) + 4u * lj + (i & 3);
-        if (row < rowsA && col < N) {
-          const float v = acc[r][c][i] * scale;
-          if (OUT == 0)
-            static_cast<float*>(C)[(crow0 + row) * N + col] = v;
-          else
-            static_cast<uint16_t*>(C)[(crow0 + row) * N + col] = f32_to_bf16(v);
         }
       }
     }
+    if (!has_next) break;
+    cur = nxt;
+    v = vn;
+    g += KT;
   }
+  // No copy into LDS may still be in flight when the workgroup's LDS is
+  // released (the zero-fill copies of the last iterations).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, bool PERSIST>
 hipError_t launch(dim3 grid, int out_dtype, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                   const float* tsA, const float* tsB, void* C, uint32_t M, uint32_t N, uint32_t K, uint32_t tilesM,
                   uint32_t tilesN, const Groups& gp, hipStream_t stream) {
   if (out_dtype == 0)
-    gemm_kernel<FMT, 0, GROUPED><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
+    gemm_kernel<FMT, 0, GROUPED, PERSIST><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
   else
-    gemm_kernel<FMT, 1, GROUPED><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
+    gemm_kernel<FMT, 1, GROUPED, PERSIST><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, tilesN, gp);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Workgroups that a persistent launch keeps resident: one per compute unit
+// (a multiple of 8, so that each workgroup stays on one XCD).  Cached per
+// device; the value never changes, so concurrent first calls are harmless.
+static uint32_t resident_workgroups() {
+  static std::atomic<uint32_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256u;
+  uint32_t n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0u) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+    n = (uint32_t)cus / 8u * 8u;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Grid for `tiles` tiles of K/256 stages: every tile its own workgroup when
+// there is a single stage (nothing to overlap) or when not `persistent`, else
+// at most one resident wave of workgroups that walk the tiles (a persistent
+// kernel given one workgroup per tile finds no next tile and stops after one).  Measured:
+// walking the tiles (the next tile's first stages copied during this one's
+// last iterations, C stored from registers) helps the NVFP4 GEMM (4096 x
+// 14336 x 4096: +5%) and the grouped GEMM (MoE: +8%); the dense MXFP4 GEMM is
+// faster one tile per workgroup with C stored through LDS (8192^3: 3709 vs
+// 3670 TFLOP/s).
+static uint32_t tiled_grid(uint64_t tiles, int64_t K, bool persistent) {
+  const uint64_t KT = (uint64_t)((K + 255) / 256);
+  if (KT < 2u || !persistent) return (uint32_t)tiles;
+  const uint64_t g = resident_workgroups();
+  return (uint32_t)(tiles < g ? tiles : g);
+}
+
 hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                              const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                              int out_dtype, hipStream_t stream) {
   const uint32_t tilesM = (uint32_t)((M + BM - 1) / BM), tilesN = (uint32_t)((N + BN - 1) / BN);
-  const dim3 grid(tilesM * tilesN);
+  const dim3 grid(tiled_grid((uint64_t)tilesM * tilesN, K, fmt == kFmtNV));
   const Groups none{nullptr, nullptr, 0, 0, 0, 0};
   if (fmt == kFmtNV)
-    return launch<kFmtNV, false>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
+    return launch<kFmtNV, false, true>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
                                  tilesM, tilesN, none, stream);
-  return launch<kFmtMX, false>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
+  return launch<kFmtMX, false, false>(grid, out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)M, (uint32_t)N, (uint32_t)K,
                                tilesM, tilesN, none, stream);
 }
 
@@ -502,12 +624,12 @@ hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_ro
   // multiple of 8 so the XCD-contiguous order covers every tile; workgroups
   // past the real count return at once.
   const uint64_t max_tiles = ((uint64_t)(total_rows + BM - 1) / BM + (uint64_t)E) * tilesN;
-  const uint64_t grid = (max_tiles + 7) / 8 * 8;
+  const uint64_t grid = tiled_grid((max_tiles + 7) / 8 * 8, K, true);
   const uint32_t KT = (uint32_t)((K + 255) / 256);
   const size_t scale_stride = (size_t)((N + 31) / 32) * KT * (fmt == kFmtNV ? 512u : 256u);
   const Groups gp{row_idx, group_off, E, (uint32_t)A_rows, (size_t)N * (size_t)(K / 2), scale_stride};
   (void)fmt;
-  return launch<kFmtMX, true>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)total_rows,
+  return launch<kFmtMX, true, true>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)total_rows,
                               (uint32_t)N, (uint32_t)K, 0, tilesN, gp, stream);
 }
 
