@@ -1,12 +1,14 @@
 """Benchmark of the FP4 block-scaled quantise / GEMM path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--only NAME] [--no-cpu-baseline]
 
 Prints ONE JSON line.  The headline (`value`) is the 8192^3 MXFP4 GEMM: A and B
 N(0,1) with 0.2% outliers x20, pre-quantised to 32-blocks with E8M0 scales,
 FP32 accumulation, BF16 output; one step = one GEMM; exactly K timed steps
 after W warm-up steps, with 8 rotating copies of the operands so repeated
-steps are not served from the 256 MB Infinity Cache.  The same line carries
+steps are not served from the 256 MB Infinity Cache.  Before each workload's
+warm-up its step runs untimed for --settle seconds (default 0.25) so that the
+GPU's clocks have reached their sustained level under load.  The same line carries
 the dominant kernel's roofline (HIP events around the timed launches, on the
 launch stream), the CPU oracle timed on a bounded sample of the same
 workload, and, under "workloads", the other measured workloads:
@@ -69,9 +71,22 @@ def arithmetic_intensity(M, N, K, block=32, out_bytes=2, include_c=True):
 
 
 # ---- timing helpers ---------------------------------------------------------
+SETTLE_S = 0.25
+
+
 def time_steps(torch, step, steps, warmup):
-    """Run `warmup` untimed steps, then time exactly `steps` steps with HIP
-    events on the current (launch) stream.  Returns ms per step."""
+    """Run the step untimed for SETTLE_S seconds (the GPU's clocks need tens of
+    milliseconds under load to reach their sustained level: with 10 warm-up
+    8192^3 GEMMs alone the timed ones ran 10% slower), then `warmup` untimed
+    steps, then time exactly `steps` steps with HIP events on the current
+    (launch) stream.  Returns ms per step."""
+    i = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(4):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -311,6 +326,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--only", default=None, help="run only the headline (mxfp4_gemm_8192) or one other workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="seconds of untimed steps before each workload's warm-up (clock ramp)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device copy (x*1 -> y) 3 times, to scale the HBM byte counters")
     return p.parse_args()
@@ -342,6 +359,8 @@ def main():
         calibrate_copy(torch)
         return
     t_start = time.perf_counter()
+    global SETTLE_S
+    SETTLE_S = args.settle
 
     head = mxfp4_gemm_8192(torch, fp4, synth, args)
     sys.stderr.write("[bench] mxfp4_gemm_8192 %.4f ms %.1f TFLOP/s\n" % (head["ms"], head["tflops"]))
@@ -374,7 +393,8 @@ def main():
         "dtype": "mxfp4", "data": "synthetic",
         "config": {"workload": "mxfp4_gemm_8192x8192x8192", "M": 8192, "N": 8192, "K": 8192,
                    "operands": "pre-quantised MXFP4 (E2M1 codes, E8M0 32-blocks), N(0,1) with 0.2% outliers x20",
-                   "out": "bf16", "accumulate": "fp32", "parallelism": "single-gpu", "rotating_copies": ROTATE},
+                   "out": "bf16", "accumulate": "fp32", "parallelism": "single-gpu", "rotating_copies": ROTATE,
+                   "settle_s": SETTLE_S},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_FP4_TFLOPS, 4), "traffic": traffic_record(kernel_src),
                      "kernel": "gemm_kernel<MXFP4, BF16, dense>",
