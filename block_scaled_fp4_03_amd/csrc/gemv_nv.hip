@@ -39,7 +39,8 @@ namespace {
 //         ([tile][sub-step][lane] x 16 B) and the scale tiles verbatim; each
 //         MFMA decodes its A operand.  Rows >= M are zero codes.
 // At the end of a row block the 16 waves' partial sums are added in a fixed
-// order through LDS (deterministic); no exchange between workgroups and no
+// order through LDS (deterministic): for M <= 8 all at once after one
+// barrier, otherwise in three rounds.  No exchange between workgroups and no
 // workspace.
 // ---------------------------------------------------------------------------
 constexpr uint32_t GV_WAVES = 16;               // wavefronts per workgroup (K split)
@@ -148,28 +149,52 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- weight ring prologue
+  // ---- weight ring prologue.  Work item j of this wave is tile
+  // kt = wave + 16 (j % NJ) of row block blockIdx.x + (j / NJ) gridDim.x.
+  // PD = 1: the ring holds one tile, refilled one 64-value sub-step at a
+  // time: once sub-step s of item j is multiplied, sub-step s of item j + 1
+  // is requested into the same registers (its scales with sub-step 0), so
+  // the weights stream without a pause while item j is computed.
+  static_assert(PD == 1, "the sub-step ring holds one tile");
   const uint32_t lane_off = li * ldb + 16u * lj;
-  GvTile ring[PD];
-  auto issue = [&](GvTile& d, uint32_t j) {
+  struct TileSrc {
+    __amdgpu_buffer_rsrc_t rw, rsw;
+    uint32_t off;    // this lane's code offset of the tile (out of range if none)
+    uint32_t soff;   // this lane's scale offset
+  };
+  // Item j's sources; past the last item, out-of-range offsets (the loads
+  // return zeros without touching memory), so that every iteration issues
+  // the same loads into the same registers.
+  auto tile_src = [&](uint32_t j) {
     const uint32_t rb = blockIdx.x + (j / NJ) * gridDim.x;
     const uint32_t kt = wave + GV_WAVES * (j % NJ);
     const uint32_t n0 = rb * 32u;
-    const uint32_t rows = __builtin_amdgcn_readfirstlane(N - n0 < 32u ? N - n0 : 32u);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)n0 * ldb, rows * ldb);
-    const __amdgpu_buffer_rsrc_t rsw = make_rsrc(sW + (size_t)rb * srow, srow);
-    const bool ok = kt < KT;
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t off = ok ? lane_off + kt * 128u + 32u * s2 : 0x80000000u;
-      d.w[s2] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
-    }
-    d.ws = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsw, ok ? kt * 512u + 8u * lane : 0x80000000u,
-                                                                          0, 0));
+    const bool item = j < T;              // else rb may lie past the last row block: empty ranges
+    const uint32_t rows = __builtin_amdgcn_readfirstlane(item ? (N - n0 < 32u ? N - n0 : 32u) : 0u);
+    TileSrc t;
+    t.rw = make_rsrc(W + (size_t)n0 * ldb, rows * ldb);
+    t.rsw = make_rsrc(sW + (size_t)rb * srow, item ? srow : 0u);
+    const bool ok = kt < KT && item;
+    t.off = ok ? lane_off + kt * 128u : 0x80000000u;
+    t.soff = ok ? kt * 512u + 8u * lane : 0x80000000u;
+    return t;
   };
+  auto load_codes = [&](const TileSrc& t, int s2) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(t.rw, t.off + 32u * (uint32_t)s2, 0, 0));
+  };
+  auto load_scales = [&](const TileSrc& t) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(t.rsw, t.soff, 0, 0));
+  };
+  // Issued unconditionally (out of range when T == 0): on both paths the
+  // same loads follow the activation's, so the waits for the activation
+  // below count past them and do not wait for the weights.
+  GvTile cur;
+  {
+    const TileSrc t0 = tile_src(0);
+    cur.ws = load_scales(t0);   // scales first, as in the loop (the same wait counts on entry)
 #pragma unroll
-  for (int p = 0; p < PD; ++p)
-    if ((uint32_t)p < T) issue(ring[p], p);
+    for (int s2 = 0; s2 < 4; ++s2) cur.w[s2] = load_codes(t0, s2);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- activation -> LDS
@@ -270,22 +295,31 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
   // AF16: lanes of rows >= M read a 512-byte zero block at a fixed place.
   const uint32_t a_row_off = li * RS + 64u * lj;
   v16f acc0 = v16f{}, acc1 = v16f{};
-  for (uint32_t jj = 0; jj < T; jj += PD) {
-#pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const uint32_t j = jj + p;
-      if (j >= T) break;
+  {
+    for (uint32_t j = 0; j < T; ++j) {
       const uint32_t kt = wave + GV_WAVES * (j % NJ);
-      if (kt < KT) {
-        const GvTile& d = ring[p];
-        const uint32_t abase = li < M ? a_row_off + kt * 512u : zero_off;
-        u32x2 as2 = u32x2{};
-        if (AMODE == kACode) as2 = *reinterpret_cast<const u32x2*>(lds_a + KT * 4096u + kt * 512u + 8u * lane);
+      const TileSrc tn = tile_src(j + 1u);
+      // The tile's scales (bytes 2 s2 and 2 s2 + 1 of sub-step s2: blocks of
+      // code words 0, 1 and 2, 3), converted before their registers take
+      // item j + 1's.
+      v2h wsp[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          // scale bytes 2*s2 (blocks of words 0, 1) and 2*s2 + 1 (words 2, 3)
-          const v2h wsp = (s2 & 1) ? e4m3x2_to_f16<true>(d.ws[s2 >> 1]) : e4m3x2_to_f16<false>(d.ws[s2 >> 1]);
-          const v2h w0 = splat_lo(wsp), w1 = splat_hi(wsp);
+      for (int s2 = 0; s2 < 4; ++s2)
+        wsp[s2] = (s2 & 1) ? e4m3x2_to_f16<true>(cur.ws[s2 >> 1]) : e4m3x2_to_f16<false>(cur.ws[s2 >> 1]);
+      // The conversions stay ahead of the new load (the empty asm takes their
+      // results), so that the new scales reuse the old ones' registers: a
+      // copy at the loop's end would wait for the load.
+      asm volatile("" : : "v"(wsp[0]), "v"(wsp[1]), "v"(wsp[2]), "v"(wsp[3]));
+      cur.ws = load_scales(tn);
+      const bool live = kt < KT;
+      const uint32_t abase = li < M ? a_row_off + kt * 512u : zero_off;
+      u32x2 as2 = u32x2{};
+      if (AMODE == kACode && live) as2 = *reinterpret_cast<const u32x2*>(lds_a + KT * 4096u + kt * 512u + 8u * lane);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        GvTile& d = cur;
+        if (live) {
+          const v2h w0 = splat_lo(wsp[s2]), w1 = splat_hi(wsp[s2]);
           v4i acodes = v4i{};
           v2h a0 = v2h{}, a1 = v2h{};
           if (AMODE == kACode) {
@@ -308,57 +342,86 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
               acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc0, 0, 0, 0);
           }
         }
+        // Sub-step s2 is decoded: its registers take item j + 1's.
+        d.w[s2] = load_codes(tn, s2);
       }
-      if (j + PD < T) issue(ring[p], j + PD);
 
       if (j % NJ == NJ - 1u) {
-        // End of a row block: waves 0..3 gather waves 4..15 (in order of w),
-        // then wave 0 gathers 1..3, scales and stores.  Lane L holds column
-        // n0 + L%32 and rows 8(i/4) + 4(L/32) + i%4.
+        // End of a row block.  Lane L holds column n0 + L%32 and rows
+        // 8(i/4) + 4(L/32) + i%4 of the wave's partial sums.
         const uint32_t n0 = (blockIdx.x + (j / NJ) * gridDim.x) * 32u;
         v16f acc = acc0 + acc1;
+        if (M <= 8u) {
+          // Rows < 8 sit in registers 0-3: all 16 waves' partials fit the
+          // slots at once ([wave][row][column]); one barrier, then thread
+          // (row, column) adds them in wave order, scales and stores.
+          float(*part)[8][32] = reinterpret_cast<float(*)[8][32]>(&red[0][0][0]);
 #pragma unroll
-        for (uint32_t r = 1; r < GV_WAVES / 4u; ++r) {
-          if (wave / 4u == r) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
-              if (m < M) red[wave & 3u][m][li] = acc[i];
-            }
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t m = 4u * lj + (uint32_t)i;
+            if (m < M) part[wave][m][li] = acc[i];
           }
           __syncthreads();
-          if (wave < 4u) {
+          if (tid < 32u * M) {
+            const uint32_t m = tid >> 5, c = tid & 31u, col = n0 + c;
+            float v = part[0][m][c];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
-              if (m < M) acc[i] += red[wave][m][li];
-            }
-          }
-          __syncthreads();
-        }
-        if (wave >= 1u && wave < 4u) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
-            if (m < M) red[wave][m][li] = acc[i];
-          }
-        }
-        __syncthreads();
-        if (wave == 0) {
-          const uint32_t col = n0 + li;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
-            if (m < M && col < N) {
-              const float v = (((acc[i] + red[1][m][li]) + red[2][m][li]) + red[3][m][li]) * scale;
+            for (uint32_t w = 1; w < GV_WAVES; ++w) v += part[w][m][c];
+            v *= scale;
+            if (col < N) {
               if (OUT == 0)
                 static_cast<float*>(C)[(size_t)m * N + col] = v;
               else
                 static_cast<uint16_t*>(C)[(size_t)m * N + col] = f32_to_bf16(v);
             }
           }
+          if (j + 1u < T) __syncthreads();   // the slots are reused by the next row block
+        } else {
+          // Waves 0..3 gather waves 4..15 (in order of w), then wave 0
+          // gathers 1..3, scales and stores.
+#pragma unroll
+          for (uint32_t r = 1; r < GV_WAVES / 4u; ++r) {
+            if (wave / 4u == r) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+                if (m < M) red[wave & 3u][m][li] = acc[i];
+              }
+            }
+            __syncthreads();
+            if (wave < 4u) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+                if (m < M) acc[i] += red[wave][m][li];
+              }
+            }
+            __syncthreads();
+          }
+          if (wave >= 1u && wave < 4u) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+              if (m < M) red[wave][m][li] = acc[i];
+            }
+          }
+          __syncthreads();
+          if (wave == 0) {
+            const uint32_t col = n0 + li;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+              if (m < M && col < N) {
+                const float v = (((acc[i] + red[1][m][li]) + red[2][m][li]) + red[3][m][li]) * scale;
+                if (OUT == 0)
+                  static_cast<float*>(C)[(size_t)m * N + col] = v;
+                else
+                  static_cast<uint16_t*>(C)[(size_t)m * N + col] = f32_to_bf16(v);
+              }
+            }
+          }
+          __syncthreads();
         }
-        __syncthreads();
         acc0 = v16f{};
         acc1 = v16f{};
       }
