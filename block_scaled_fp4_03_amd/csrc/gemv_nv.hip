@@ -40,8 +40,9 @@ namespace {
 //         MFMA decodes its A operand.  Rows >= M are zero codes.
 // At the end of a row block the 16 waves' partial sums are added in a fixed
 // order through LDS (deterministic): for M <= 8 all at once after one
-// barrier, otherwise in three rounds.  No exchange between workgroups and no
-// workspace.
+// barrier; for larger M likewise in the workgroup's last row block (in the
+// then dead activation staging area), otherwise in three rounds.  No exchange
+// between workgroups and no workspace.
 // ---------------------------------------------------------------------------
 constexpr uint32_t GV_WAVES = 16;               // wavefronts per workgroup (K split)
 // Weight tiles in flight per wave (ring depth), both paths.  Depth 1 measured
@@ -376,6 +377,31 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
             }
           }
           if (j + 1u < T) __syncthreads();   // the slots are reused by the next row block
+        } else if (j + 1u == T) {
+          // The workgroup's last row block: the activation staging is dead, so
+          // all 16 waves' partials ([wave][row][column], 64 KB) go there at
+          // once; one barrier, then thread (row, column) adds them in wave
+          // order, scales and stores.
+          static_assert(GV_WAVES * 32u * 32u * 4u <= GV_A_BYTES, "partials fit the staging area");
+          float(*part)[32][32] = reinterpret_cast<float(*)[32][32]>(lds_a);
+          __syncthreads();   // every wave is done reading the staged activation
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t m = 8u * (i >> 2) + 4u * lj + (i & 3);
+            if (m < M) part[wave][m][li] = acc[i];
+          }
+          __syncthreads();
+          const uint32_t m = tid >> 5, c = tid & 31u, col = n0 + c;
+          if (m < M && col < N) {
+            float v = part[0][m][c];
+#pragma unroll
+            for (uint32_t w = 1; w < GV_WAVES; ++w) v += part[w][m][c];
+            v *= scale;
+            if (OUT == 0)
+              static_cast<float*>(C)[(size_t)m * N + col] = v;
+            else
+              static_cast<uint16_t*>(C)[(size_t)m * N + col] = f32_to_bf16(v);
+          }
         } else {
           // Waves 0..3 gather waves 4..15 (in order of w), then wave 0
           // gathers 1..3, scales and stores.

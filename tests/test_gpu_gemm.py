@@ -271,12 +271,14 @@ def test_nvfp4_decode_gemv_repeated_calls(orc):
         assert_gemm_close(orc, to_host(C), Cref, T, False, "gemv repeated M=%d" % M)
 
 
-def test_nvfp4_decode_many_row_blocks(orc):
+@pytest.mark.parametrize("M,N,K", [(3, 1024 * 32 + 40, 288), (20, 1024 * 32 + 40, 288), (32, 300 * 32 + 8, 4352)])
+def test_nvfp4_decode_many_row_blocks(orc, M, N, K):
     """More 32-row weight blocks than the decode grid holds (grid-stride loop),
-    a ragged last block and a ragged K tail."""
+    a ragged last block and a ragged K tail.  M <= 8 reduces in one round
+    everywhere; larger M in three rounds except in a workgroup's last row
+    block, so both reductions run in one launch."""
     import torch
-    M, N, K = 3, 1024 * 32 + 40, 288
-    a = synth.gaussian(81, (M, K))
+    a = synth.gaussian(81 + M, (M, K))
     b = synth.gaussian(82, (N, K), std=0.02, bernoulli=0.002)
     say("gemv many row blocks M=%d N=%d K=%d" % (M, N, K))
     qa, ra = _quant_both(orc, a, 1)
