@@ -68,6 +68,8 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
     if (!aligned(workspace, 4)) return FP4_ERR_ALIGN;
   }
   hipStream_t s = as_stream(stream);
+  if (compute_ts && fp4::quantize_nv_small_applies(rows, K, in_dtype))
+    return launched(fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, s));
   if (compute_ts) {
     int rc = launched(fp4::launch_tensor_amax(x, in_dtype, rows * K, static_cast<uint32_t*>(workspace), tensor_scale, s));
     if (rc != FP4_OK) return rc;

@@ -15,6 +15,7 @@
 // shuffles into the dwords of the tiled layout, so every store is a dword.
 #include "fp4_device.h"
 #include "fp4_launch.h"
+#include "gemm_common.h"
 
 #include <float.h>
 
@@ -152,26 +153,28 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
 //   code = E2M1(x / d)   (x / inf = +-0 when sb == 0, so the block is all zero)
 // All divisions are IEEE FP32 round-to-nearest-even.
 // ---------------------------------------------------------------------------
+// One wave: 512 values (two scale tiles) of one row.  The lane's 8 values
+// (zeros past the matrix), then their quantisation with tensor scale s_t.
 template <int DT>
-__global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales,
-                                                          const float* __restrict__ tensor_scale, uint32_t rows,
-                                                          uint32_t K, uint32_t KT, uint32_t KT2,
-                                                          uint32_t total_waves) {
-  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
-  const uint32_t lane = threadIdx.x & 63u;
-  if (wave >= total_waves) return;
+__device__ __forceinline__ bool load_nv_wave(const void* __restrict__ x, uint32_t rows, uint32_t K, uint32_t KT2,
+                                             uint32_t wave, uint32_t lane, float v[8]) {
   const uint32_t row = wave / KT2, kt2 = wave % KT2;
   const uint32_t k0 = kt2 * 512u + lane * 8u;
   const bool valid = row < rows && k0 < K;
-  const float s_t = *tensor_scale;
-  float v[8];
   if (valid) {
     load8v<DT>(x, (size_t)row * K + k0, v);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = 0.0f;
   }
+  return valid;
+}
+
+__device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, float s_t, uint32_t K, uint32_t KT,
+                                                 uint32_t KT2, uint32_t wave, uint32_t lane) {
+  const uint32_t row = wave / KT2, kt2 = wave % KT2;
+  const uint32_t k0 = kt2 * 512u + lane * 8u;
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
@@ -206,6 +209,105 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
     const size_t off = ((size_t)(row >> 5) * KT + kt) * 512u + (32u * j + (row & 31u)) * 8u + 4u * d;
     *reinterpret_cast<uint32_t*>(scales + off) = dw;
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ tensor_scale, uint32_t rows,
+                                                          uint32_t K, uint32_t KT, uint32_t KT2,
+                                                          uint32_t total_waves) {
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  if (wave >= total_waves) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  float v[8];
+  const bool valid = load_nv_wave<DT>(x, rows, K, KT2, wave, lane, v);
+  quantize_nv_wave(v, valid, codes, scales, *tensor_scale, K, KT, KT2, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantiser for small tensors (the activation of a decode step): every
+// workgroup of 16 waves reduces the whole tensor's maximum itself (exact, so
+// the same s_t as tensor_amax_kernel; the input stays in L2 after the first
+// reads), then its waves quantise their own 512-value pieces as above.  One
+// launch instead of two and no cross-workgroup exchange; workgroup 0 writes
+// s_t.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNvSmallMaxBytes = 256u * 1024u;
+
+template <int DT>
+__global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __restrict__ x,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ tensor_scale, size_t n8,
+                                                                 uint32_t rows, uint32_t K, uint32_t KT,
+                                                                 uint32_t KT2, uint32_t total_waves) {
+  __shared__ float red[16];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+  constexpr uint32_t EB = DT == kDtF32 ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)(n8 * 8u * EB));
+  // This wave's own values first (they arrive while the maximum is reduced);
+  // branch-free, so that nothing waits for them before the loads below.
+  const uint32_t wave = blockIdx.x * 16u + w;
+  const uint32_t row = wave / KT2, k0 = (wave % KT2) * 512u + lane * 8u;
+  const bool valid = wave < total_waves && row < rows && k0 < K;
+  const uint32_t voff = valid ? (row * K + k0) * EB : 0x80000000u;
+  u32x4 own[EB / 2u];
+#pragma unroll
+  for (uint32_t h = 0; h < EB / 2u; ++h)
+    own[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + 16u * h, 0, 0));
+  // Loads in batches of 8 chunks (of 8 values) per thread, all issued before
+  // their use; at most 256 KB means at most 2 batches.  Buffer loads past the
+  // end return zeros (no branch, so the batch stays in flight together).
+  float m = 0.0f;
+  for (uint32_t b = tid; b < (uint32_t)n8; b += 8u * 1024u) {
+    u32x4 raw[8][EB / 2u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (uint32_t h = 0; h < EB / 2u; ++h)
+        raw[u][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (b + (uint32_t)u * 1024u) * 8u * EB + 16u * h, 0, 0));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (uint32_t h = 0; h < EB / 2u; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t wd = raw[u][h][k];
+          if (DT == kDtF32) {
+            m = fmaxf(m, fabsf(u2f(wd)));
+          } else {
+            m = fmaxf(m, fabsf(u2f(wd << 16)));
+            m = fmaxf(m, fabsf(u2f(wd & 0xFFFF0000u)));
+          }
+        }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0u) red[w] = m;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) amax = fmaxf(amax, red[i]);
+  float s_t = 1.0f;
+  if (amax > 0.0f) {
+    s_t = amax / 2688.0f;
+    if (s_t < FLT_MIN) s_t = FLT_MIN;
+  }
+  if (blockIdx.x == 0 && tid == 0) *tensor_scale = s_t;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (DT == kDtF32) {
+      v[k] = u2f(own[0][k]);
+      v[4 + k] = u2f(own[EB / 2u - 1u][k]);
+    } else {
+      v[2 * k] = u2f(own[0][k] << 16);
+      v[2 * k + 1] = u2f(own[0][k] & 0xFFFF0000u);
+    }
+  }
+  if (wave < total_waves) quantize_nv_wave(v, valid, codes, scales, s_t, K, KT, KT2, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,6 +371,28 @@ hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* 
     tensor_amax_kernel<kDtF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
   else
     tensor_amax_kernel<kDtBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
+  return hipGetLastError();
+}
+
+bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype) {
+  const int64_t bytes = rows * K * (in_dtype == kDtF32 ? 4 : 2);
+  return rows >= 1 && K >= 16 && bytes <= (int64_t)kNvSmallMaxBytes;
+}
+
+hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                    float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
+  const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
+  const uint32_t waves = rows_pad * KT2;
+  const dim3 grid((waves + 15u) / 16u);
+  const size_t n8 = (size_t)rows * (size_t)K / 8u;
+  if (in_dtype == kDtF32)
+    quantize_nv_small_kernel<kDtF32><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k, KT,
+                                                                     KT2, waves);
+  else
+    quantize_nv_small_kernel<kDtBF16><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k, KT,
+                                                                      KT2, waves);
   return hipGetLastError();
 }
 

@@ -122,6 +122,10 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
  *   codes and block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
  *   is ignored for MXFP4.  NVFP4 without FP4_TS_GIVEN needs a workspace of
  *   fp4_workspace_size(FP4_OP_QUANTIZE, ...) bytes; otherwise workspace may be NULL.
+ *   (Inputs of at most 256 KB take a single launch in which every workgroup
+ *   reduces the maximum itself and the workspace is left untouched; larger ones
+ *   reduce across workgroups through the workspace, then quantise.  Both give
+ *   the same bits.)
  * rows == 0 or K == 0 is a no-op. */
 int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,

@@ -75,6 +75,20 @@ def test_nvfp4_all_zero_tensor(orc):
     assert ts == 1.0
 
 
+@pytest.mark.parametrize("rows,K,bf16", [(8, 8192, True), (32, 2048, False), (32, 2064, False), (1, 16, True)])
+def test_nvfp4_single_launch_threshold(orc, rows, K, bf16):
+    """Inputs of at most 256 KB take the one-launch quantiser (each workgroup
+    reduces the whole maximum), larger ones the two-launch path: (32, 2048)
+    FP32 is exactly 256 KB, (32, 2064) FP32 one block more.  The maximum sits
+    in the last element, so a workgroup that skipped any part would get s_t
+    wrong."""
+    x = synth.gaussian(23 + rows, (rows, K))
+    x[-1, -1] = 777.0
+    if bf16:
+        x = synth.to_bf16_bits(x)
+    _run(orc, 1, x)
+
+
 def test_nvfp4_tensor_scale_on_large_tensor(orc):
     # many workgroups contribute to the amax; the maximum sits in the last row
     x = synth.gaussian(21, (4096, 1024), every=4099)
