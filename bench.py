@@ -26,6 +26,8 @@ workload, and, under "workloads", the other measured workloads:
   mxfp4_256               A, B 256x256 FP32; step = quantise A, B + GEMM (FP32
                           out); microseconds.
   mxfp4_quantize_8192     8192x8192 FP32 -> MXFP4; GB/s.
+  mxfp4_gemm_requant_8192 the headline GEMM with bias, ReLU and MXFP4 output
+                          in the same kernel (fp4_gemm_ex); TFLOP/s.
 
 Launch-bound steps (decode, 256^3) are captured once in a HIP graph and
 replayed; every replayed result is checked against the eager one.
@@ -163,6 +165,34 @@ def mxfp4_gemm_8192(torch, fp4, synth, args):
     ms = time_steps(torch, step, args.steps, args.warmup)
     tflops = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
     return dict(ms=ms, tflops=tflops, a=a, b=b)
+
+
+def mxfp4_gemm_requant_8192(torch, fp4, synth, a, b):
+    """The 8192^3 MXFP4 GEMM with the whole epilogue in the kernel: + bias,
+    ReLU, and the result quantised again to MXFP4 along N (the next layer's
+    operand), 8 rotating operand copies as the headline."""
+    n = 8192
+    qa0 = fp4.quantize(to_dev(torch, a), fp4.MXFP4)
+    qb0 = fp4.quantize(to_dev(torch, b), fp4.MXFP4)
+    qa = [qa0] + [fp4.Quantized(qa0.codes.clone(), qa0.scales.clone(), None, fp4.MXFP4, n, n)
+                  for _ in range(ROTATE - 1)]
+    qb = [qb0] + [fp4.Quantized(qb0.codes.clone(), qb0.scales.clone(), None, fp4.MXFP4, n, n)
+                  for _ in range(ROTATE - 1)]
+    bias = torch.from_numpy((0.5 * synth.gaussian(11, (n,))).astype(np.float32)).cuda()
+    out = fp4.Quantized(torch.empty((n, n // 2), dtype=torch.uint8, device="cuda"),
+                        torch.empty(fp4.fp4_scale_bytes(fp4.MXFP4, n, n), dtype=torch.uint8, device="cuda"),
+                        None, fp4.MXFP4, n, n)
+    torch.cuda.synchronize()
+
+    def step(i):
+        fp4.gemm_ex(qa[i % ROTATE], qb[i % ROTATE], bias=bias, act=fp4.ACT_RELU, out=fp4.OUT_MXFP4, C=out)
+
+    ms = time_steps(torch, step, 30, 5)
+    tf = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
+    out_bytes = n * n // 2 + fp4.fp4_scale_bytes(fp4.MXFP4, n, n)
+    return {"ms_per_step": round(ms, 4), "TFLOP_per_s": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+            "output_bytes": int(out_bytes),
+            "step": "MXFP4 GEMM + bias + ReLU + MXFP4 re-quantisation of C in one kernel (fp4_gemm_ex)"}
 
 
 def cpu_baseline_gemm(a, b, K, budget_s=12.0):
@@ -369,8 +399,9 @@ def main():
 
     extra = {}
     a8192 = head.pop("a")
-    del head["b"]
+    b8192 = head.pop("b")
     todo = [("mxfp4_quantize_8192", lambda: mxfp4_quantize_8192(torch, fp4, a8192)),
+            ("mxfp4_gemm_requant_8192", lambda: mxfp4_gemm_requant_8192(torch, fp4, synth, a8192, b8192)),
             ("nvfp4_decode_m1", lambda: nvfp4_decode(torch, fp4, synth, 1)),
             ("nvfp4_decode_m8", lambda: nvfp4_decode(torch, fp4, synth, 8)),
             ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),

@@ -2,7 +2,7 @@
 for AMD Instinct MI355X (gfx950).
 
 The C ABI (include/fp4.h) is exposed under the same names (``fp4_quantize``,
-``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_grouped``, ``fp4_scale_bytes``,
+``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_ex``, ``fp4_gemm_grouped``, ``fp4_scale_bytes``,
 ``fp4_workspace_size``, ``fp4_status_string``), taking raw device pointers as
 integers.  The tensor helpers below only allocate outputs with torch and
 marshal ``data_ptr()`` / the current stream into those calls: every step of the
@@ -20,8 +20,11 @@ MXFP4, NVFP4, MXFP4_OCP = 0, 1, 2
 F32, BF16 = 0, 1
 OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 TS_GIVEN = 1
+# enum fp4_out / fp4_act (fp4_gemm_ex)
+OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP = 0, 1, 2, 3
+ACT_NONE, ACT_RELU = 0, 1
 
-FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_dequantize", "fp4_gemm",
+FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
              "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_status_string")
 
 
@@ -48,6 +51,7 @@ def lib():
             "fp4_quantize": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P, SZ, P]),
             "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
             "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
+            "fp4_gemm_ex": (I32, [P, P, P, P, P, P, P, I32, P, P, I64, I64, I64, I32, I32, P]),
             "fp4_gemm_grouped": (I32, [P, P, I64, P, P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_nvfp4_act": (I32, [P, I32, P, U32, P, P, P, P, I64, I64, I64, I32, P]),
             "fp4_gemm_nvfp4_act_supported": (I32, [I64, I64, I64, I32]),
@@ -86,6 +90,10 @@ def fp4_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows,
 
 def fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, workspace_bytes, stream):
     return lib().fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, workspace_bytes, stream)
+
+
+def fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, M, N, K, fmt, out, stream):
+    return lib().fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, M, N, K, fmt, out, stream)
 
 
 def fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, total_rows, N, K, fmt, out_dtype,
@@ -199,6 +207,35 @@ def gemm(a, b, out_dtype=None, out=None, ws=None, stream=None):
                   0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "fp4_gemm")
     return out
+
+
+def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
+    """C = act((A . B^T) * tsA * tsB + bias) in one kernel (see fp4_gemm_ex in
+    include/fp4.h).  out: OUT_F32 / OUT_BF16 -> an M x N tensor; OUT_MXFP4 /
+    OUT_MXFP4_OCP -> a Quantized M x N MXFP4 matrix (the next GEMM's A).
+    bias: N float32 CUDA tensor or None.  C: optional preallocated output
+    (tensor, or Quantized for FP4 output)."""
+    torch = _torch()
+    M, N, K = a.rows, b.rows, a.K
+    if b.K != K or a.fmt != b.fmt:
+        raise ValueError("operands disagree on K or format")
+    dev = a.codes.device
+    fp4_out = out in (OUT_MXFP4, OUT_MXFP4_OCP)
+    if C is None:
+        if fp4_out:
+            ofmt = MXFP4 if out == OUT_MXFP4 else MXFP4_OCP
+            nbytes = fp4_scale_bytes(ofmt, M, N)
+            if nbytes < 0:
+                raise Fp4Error(int(nbytes), "fp4_scale_bytes")
+            C = Quantized(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+                          torch.empty(nbytes, dtype=torch.uint8, device=dev), None, ofmt, M, N)
+        else:
+            C = torch.empty((M, N), dtype=torch.float32 if out == OUT_F32 else torch.bfloat16, device=dev)
+    cptr, sptr = (_ptr(C.codes), _ptr(C.scales)) if fp4_out else (_ptr(C), None)
+    rc = fp4_gemm_ex(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(a.tensor_scale),
+                     _ptr(b.tensor_scale), _ptr(bias), act, cptr, sptr, M, N, K, a.fmt, out, _stream(stream))
+    _check(rc, "fp4_gemm_ex")
+    return C
 
 
 def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_scale=None, out_dtype=None,

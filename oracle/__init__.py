@@ -68,6 +68,7 @@ def lib():
             "oracle_quantize": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32]),
             "oracle_dequantize": (None, [P, P, P, I32, P, I32, I64, I64]),
             "oracle_gemm": (None, [P, P, P, P, D, D, I64, I64, I64, I32, P, P]),
+            "oracle_epilogue": (None, [P, P, I32, I64, I64, P]),
             "oracle_gemm_sampled": (None, [P, P, P, P, D, D, I64, I64, I64, I32, P, P, I64, P, P]),
             "oracle_gemm_grouped_sampled": (None, [P, P, I64, P, P, I32, P, P, D, D, I64, I64, I32,
                                                    P, P, I64, P, P]),
@@ -194,6 +195,23 @@ def gemm(A, sA, B, sB, M, N, K, fmt, tsA=1.0, tsB=1.0):
     T = np.empty((M, N), np.float64)
     lib().oracle_gemm(_p(A), _p(sA), _p(B), _p(sB), float(tsA), float(tsB), M, N, K, fmt, _p(C), _p(T))
     return C, T
+
+
+ACT_NONE, ACT_RELU = 0, 1
+
+
+def epilogue(C, bias=None, act=ACT_NONE):
+    """Epilogue of the scaled product C (float64, M x N): C + bias[n] summed in
+    FP64 and rounded once to FP32, then ReLU (v > 0 ? v : +0) if act.  Returns
+    float32 (M, N); quantise it with quantize(...) for an FP4 output."""
+    C = np.ascontiguousarray(C, np.float64)
+    M, N = C.shape
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    if b is not None and b.shape != (N,):
+        raise ValueError("bias must have N entries")
+    out = np.empty((M, N), np.float32)
+    lib().oracle_epilogue(_p(C), _p(b), int(act), M, N, _p(out))
+    return out
 
 
 def gemm_sampled(A, sA, B, sB, M, N, K, fmt, rows, cols, tsA=1.0, tsB=1.0):

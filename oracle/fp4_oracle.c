@@ -398,6 +398,29 @@ void oracle_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
         }
 }
 
+/* ------------------------------------------------------------------ */
+/* Epilogue ([P1] §3.2: the FP32 result is multiplied by the scales, the
+ * bias is added, the activation applied, and the value converted to FP4
+ * if wanted; §4.2: C = (A_fp4 * B_fp4) * (scaleA * scaleB) + bias).  From
+ * the scaled product Cref (FP64, as oracle_gemm returns it):
+ *   v = Cref[m,n] + bias[n]   (bias NULL: no addition, so -0 stays -0),
+ *       summed in FP64 and rounded once to FP32;
+ *   act 1 (ReLU, the pages leave the function unnamed): v > 0 ? v : +0,
+ *       so -0 becomes +0.
+ * An FP4 output is then oracle_quantize of v (rows M, K = N).           */
+/* ------------------------------------------------------------------ */
+void oracle_epilogue(const double* C, const float* bias, int act, int64_t M, int64_t N, float* out)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = C[m * N + n];
+            if (bias) v += (double)bias[n];
+            float f = (float)v;
+            if (act == 1) f = f > 0.0f ? f : 0.0f;
+            out[m * N + n] = f;
+        }
+}
+
 /* Only the listed output elements (rows[i], cols[i]); for sampled checks at
  * sizes where the full product would take too long on the CPU. */
 void oracle_gemm_sampled(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,

@@ -177,3 +177,31 @@ def test_fused_decode_supported_shapes(L):
     assert s(33, 64, 1024, fp4.BF16) == 0
     assert s(1, 64, 48, fp4.BF16) == 0  # K % 32
     assert s(0, 64, 1024, fp4.BF16) == 0
+
+
+def test_gemm_ex_argument_errors(L):
+    """fp4_gemm_ex rejects bad arguments before any HIP call (fake pointers)."""
+    g = fp4.fp4_gemm_ex
+
+    def call(**kw):
+        a = dict(A=FAKE, sA=FAKE, B=FAKE, sB=FAKE, tsA=None, tsB=None, bias=None, act=0, C=FAKE, Cs=FAKE, M=64,
+                 N=64, K=256, fmt=0, out=2)
+        a.update(kw)
+        return g(a["A"], a["sA"], a["B"], a["sB"], a["tsA"], a["tsB"], a["bias"], a["act"], a["C"], a["Cs"], a["M"],
+                 a["N"], a["K"], a["fmt"], a["out"], None)
+
+    assert call(fmt=3) == -4
+    assert call(out=4) == -5
+    assert call(out=-1) == -5
+    assert call(act=2) == -8
+    assert call(K=48) == -2             # K % 32
+    assert call(N=48) == -2             # FP4 output needs N % 32 == 0
+    assert call(M=-1) == -2
+    assert call(M=0) == 0 and call(N=0) == 0
+    assert call(C=None) == -1
+    assert call(Cs=None) == -1          # FP4 output needs the scale buffer
+    assert call(fmt=1) == -1            # NVFP4 needs both tensor scales
+    assert call(bias=FAKE + 4) == -3    # bias 16-byte aligned
+    assert call(C=FAKE + 4) == -3       # FP4 output codes 16-byte aligned
+    assert call(Cs=FAKE + 2) == -3
+    assert call(A=FAKE + 8) == -3

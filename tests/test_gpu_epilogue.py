@@ -1,0 +1,183 @@
+"""The GEMM epilogue inside the kernel (fp4_gemm_ex; "Rubin FP4 GEMM deep
+dive" §3.2, §4.2): scaled FP32 result + bias, ReLU, then FP32, BF16 or the
+product quantised again to MXFP4 along N.
+
+- FP32 / BF16 outputs against the oracle (its FP64 product plus the epilogue):
+  within 1e-5 * sum|ab| of the product, widened by one FP32 rounding for the
+  bias addition (and the BF16 rounding); BF16 equals torch's cast of the FP32
+  output bit for bit.
+- MXFP4 output, exact: on data whose partial sums are all exact in FP32 the
+  output equals the oracle's quantisation of its epilogue value bit for bit.
+- MXFP4 output, any data: equals fp4_gemm (FP32) -> + bias, ReLU (torch, FP32)
+  -> fp4_quantize bit for bit, padding included (the unfused path, each part
+  of which is checked against the oracle elsewhere)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant(orc, x, fmt):
+    import block_scaled_fp4_03_amd as fp4
+    q = fp4.quantize(to_dev(x), fmt)
+    ref = orc.quantize(x, fmt)
+    np.testing.assert_array_equal(to_host(q.codes), ref[0])
+    np.testing.assert_array_equal(to_host(q.scales), ref[1])
+    return q, ref
+
+
+def _operands(orc, fmt, M, N, K, seed):
+    a = synth.gaussian(seed, (M, K), every=509 if M * K >= 509 else None)
+    b = synth.gaussian(seed + 1, (N, K), std=0.05, bernoulli=0.002)
+    return _quant(orc, a, fmt), _quant(orc, b, fmt)
+
+
+def _bias(N, seed):
+    return (0.5 * synth.gaussian(seed, (N,))).astype(np.float32)
+
+
+def _unfused_fp4(qa, qb, bias, act, out):
+    """fp4_gemm (FP32) -> + bias, ReLU in torch (FP32) -> fp4_quantize."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    v = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    if bias is not None:
+        v = v + bias
+    if act == fp4.ACT_RELU:
+        v = torch.where(v > 0, v, torch.zeros_like(v))
+    return fp4.quantize(v.contiguous(), fp4.MXFP4 if out == fp4.OUT_MXFP4 else fp4.MXFP4_OCP)
+
+
+def _fused_fp4(qa, qb, bias, act, out):
+    """fp4_gemm_ex into buffers pre-filled with 0xAB (so unwritten bytes show)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    M, N = qa.rows, qb.rows
+    ofmt = fp4.MXFP4 if out == fp4.OUT_MXFP4 else fp4.MXFP4_OCP
+    C = fp4.Quantized(torch.full((M, N // 2), 0xAB, dtype=torch.uint8, device="cuda"),
+                      torch.full((fp4.fp4_scale_bytes(ofmt, M, N),), 0xAB, dtype=torch.uint8, device="cuda"),
+                      None, ofmt, M, N)
+    return fp4.gemm_ex(qa, qb, bias=bias, act=act, out=out, C=C)
+
+
+def _interval(orc, Cref, T, bias, act):
+    """[lo, hi] of an acceptable FP32 epilogue value: the product within
+    1e-5 * T, plus bias, widened by one FP32 rounding, then ReLU."""
+    lo, hi = Cref - 1e-5 * T, Cref + 1e-5 * T
+    if bias is not None:
+        lo, hi = lo + bias.astype(np.float64), hi + bias.astype(np.float64)
+    lo = lo - np.abs(lo) * 2.0 ** -23
+    hi = hi + np.abs(hi) * 2.0 ** -23
+    if act:
+        lo, hi = np.maximum(lo, 0.0), np.maximum(hi, 0.0)
+    return lo, hi
+
+
+def _assert_in(x, lo, hi, what):
+    ok = (x >= lo) & (x <= hi)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError("%s: %d / %d outside; at %s got %r, allowed [%r, %r]"
+                             % (what, (~ok).sum(), ok.size, i, float(x[i]), float(lo[i]), float(hi[i])))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(0, 300, 260, 544), (0, 1, 32, 64), (0, 257, 513, 2880), (1, 300, 200, 1024),
+                                       (1, 64, 96, 4096)])
+@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 0), (True, 1), (False, 1)])
+def test_float_outputs_match_oracle(orc, fmt, M, N, K, with_bias, act):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    say("epilogue float fmt=%d M=%d N=%d K=%d bias=%s act=%d" % (fmt, M, N, K, with_bias, act))
+    (qa, ra), (qb, rb) = _operands(orc, fmt, M, N, K, seed=M + 3 * N + K)
+    bias = _bias(N, 99) if with_bias else None
+    bd = None if bias is None else to_dev(bias)
+    C32 = fp4.gemm_ex(qa, qb, bias=bd, act=act, out=fp4.OUT_F32)
+    C16 = fp4.gemm_ex(qa, qb, bias=bd, act=act, out=fp4.OUT_BF16)
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, fmt, tsA=ra[3], tsB=rb[3])
+    lo, hi = _interval(orc, Cref, T, bias, act)
+    c32 = to_host(C32)
+    _assert_in(c32.astype(np.float64), lo, hi, "FP32 out")
+    if act:
+        assert not np.signbit(c32).any(), "ReLU output holds -0"
+    assert torch.equal(C16.view(torch.int16), C32.to(torch.bfloat16).view(torch.int16)), "BF16 != cast of FP32"
+    c16 = orc.bf16_bits_to_f32(to_host(C16)).astype(np.float64)
+    _assert_in(c16, lo - np.abs(lo) * 2.0 ** -8, hi + np.abs(hi) * 2.0 ** -8, "BF16 out")
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(0, 300, 288, 544), (0, 256, 256, 256), (0, 33, 64, 96), (0, 520, 544, 2880),
+                                       (1, 300, 288, 1024), (1, 64, 512, 512)])
+@pytest.mark.parametrize("out", [2, 3])
+@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 1)])
+def test_fp4_output_equals_unfused_path(orc, fmt, M, N, K, out, with_bias, act):
+    """Ragged M (rows past M in the last 32-row group: padding scale bytes 0),
+    N not a multiple of 256 (blocks past N in the last scale tile: 0)."""
+    import torch
+    say("epilogue fp4 fmt=%d M=%d N=%d K=%d out=%d bias=%s act=%d" % (fmt, M, N, K, out, with_bias, act))
+    (qa, _), (qb, _) = _operands(orc, fmt, M, N, K, seed=5 * M + N + K)
+    bd = to_dev(_bias(N, 7)) if with_bias else None
+    fused = _fused_fp4(qa, qb, bd, act, out)
+    ref = _unfused_fp4(qa, qb, bd, act, out)
+    assert torch.equal(fused.codes, ref.codes), "codes differ from the unfused path"
+    assert torch.equal(fused.scales, ref.scales), "scale bytes differ from the unfused path"
+
+
+def _grid_matrix(seed, rows, K):
+    """Values on the E2M1 grid, each 32-block holding a +-6 (so MXFP4 keeps
+    them exactly with scale 2^0): every product is a multiple of 1/4 and every
+    partial sum below 2^22 quarters is exact in FP32, in any order."""
+    g = synth.rng(seed)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    x = grid[g.integers(0, 8, (rows, K))] * np.where(g.random((rows, K)) < 0.5, -1, 1).astype(np.float32)
+    x[:, ::32] = np.float32(6.0) * np.where(g.random((rows, K // 32)) < 0.5, -1, 1)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 288, 512), (256, 512, 256), (40, 96, 1024)])
+@pytest.mark.parametrize("out,act", [(2, 1), (3, 1), (2, 0)])
+def test_fp4_output_exact_against_oracle(orc, M, N, K, out, act):
+    import block_scaled_fp4_03_amd as fp4
+    say("epilogue exact M=%d N=%d K=%d out=%d act=%d" % (M, N, K, out, act))
+    a, b = _grid_matrix(1, M, K), _grid_matrix(2, N, K)
+    qa, ra = _quant(orc, a, fp4.MXFP4)
+    qb, rb = _quant(orc, b, fp4.MXFP4)
+    g = synth.rng(3)
+    bias = (g.integers(-64, 64, N) * 0.25).astype(np.float32)       # exact in every sum here
+    fused = _fused_fp4(qa, qb, to_dev(bias), act, out)
+    Cref, _ = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, orc.FMT_MXFP4)
+    v = orc.epilogue(Cref, bias, act)
+    codes, scales, _, _ = orc.quantize(v, orc.FMT_MXFP4 if out == 2 else orc.FMT_MXFP4_OCP)
+    np.testing.assert_array_equal(to_host(fused.codes), codes)
+    np.testing.assert_array_equal(to_host(fused.scales), scales)
+
+
+def test_fp4_output_full_size_8192(orc):
+    """The 8192^3 MXFP4 workload with bias, ReLU and MXFP4 output: equal to the
+    unfused path everywhere; 4 sampled rows (every column) within the
+    quantisation bound of the oracle's epilogue value (half the widest grid gap
+    of the block, amax/3 under the ceil rule, plus the product tolerance)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    say("epilogue fp4 8192^3")
+    n = 8192
+    a, b = synth.mxfp4_8192(n)
+    qa, qb = fp4.quantize(to_dev(a), fp4.MXFP4), fp4.quantize(to_dev(b), fp4.MXFP4)
+    bias = _bias(n, 11)
+    bd = to_dev(bias)
+    fused = _fused_fp4(qa, qb, bd, fp4.ACT_RELU, fp4.OUT_MXFP4)
+    ref = _unfused_fp4(qa, qb, bd, fp4.ACT_RELU, fp4.OUT_MXFP4)
+    assert torch.equal(fused.codes, ref.codes) and torch.equal(fused.scales, ref.scales)
+    rows = np.array([0, 1, 4097, 8191])
+    deq = to_host(fp4.dequantize(fused))[rows].astype(np.float64)
+    ra = orc.quantize(a[rows], orc.FMT_MXFP4)
+    rb = orc.quantize(b, orc.FMT_MXFP4)
+    rr = np.repeat(np.arange(len(rows)), n)
+    cc = np.tile(np.arange(n), len(rows))
+    Cref, T = orc.gemm_sampled(ra[0], ra[1], rb[0], rb[1], len(rows), n, n, orc.FMT_MXFP4, rr, cc)
+    Cref, T = Cref.reshape(len(rows), n), T.reshape(len(rows), n)
+    v = np.maximum(Cref + bias.astype(np.float64), 0.0)
+    amax = np.abs(v).reshape(len(rows), n // 32, 32).max(axis=2).repeat(32, axis=1)
+    err = np.abs(deq - v)
+    assert (err <= amax / 3.0 + 1e-5 * T + 1e-30).all()
