@@ -28,6 +28,8 @@ workload, and, under "workloads", the other measured workloads:
   mxfp4_quantize_8192     8192x8192 FP32 -> MXFP4; GB/s.
   mxfp4_gemm_requant_8192 the headline GEMM with bias, ReLU and MXFP4 output
                           in the same kernel (fp4_gemm_ex); TFLOP/s.
+  nvfp4_quantize_sr_8192  8192x8192 BF16 -> NVFP4 with stochastic rounding
+                          (fp4_quantize_sr); GB/s.
 
 Launch-bound steps (decode, 256^3) are captured once in a HIP graph and
 replayed; every replayed result is checked against the eager one.
@@ -193,6 +195,24 @@ def mxfp4_gemm_requant_8192(torch, fp4, synth, a, b):
     return {"ms_per_step": round(ms, 4), "TFLOP_per_s": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
             "output_bytes": int(out_bytes),
             "step": "MXFP4 GEMM + bias + ReLU + MXFP4 re-quantisation of C in one kernel (fp4_gemm_ex)"}
+
+
+def nvfp4_quantize_sr_8192(torch, fp4, synth):
+    """8192 x 8192 BF16 gradient-like tensor (N(0, 1e-3^2), 0.1% outliers x20)
+    -> NVFP4 with its own tensor scale, elements rounded stochastically
+    (fp4_quantize_sr; amax pass + quantise pass), beside the same with
+    round-to-nearest-even."""
+    n = 8192
+    x = to_dev(torch, synth.to_bf16_bits(synth.gaussian(81, (n, n), std=1e-3, bernoulli=0.001)))
+    q = fp4.quantize(x, fp4.NVFP4, sr_seed=1)
+    ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, n, 0, n)
+    ms_sr = time_steps(torch, lambda i: fp4.quantize(x, fp4.NVFP4, ws=ws, out=q, sr_seed=i + 1), 30, 5)
+    ms_rn = time_steps(torch, lambda i: fp4.quantize(x, fp4.NVFP4, ws=ws, out=q), 30, 5)
+    nbytes = 2 * n * n * 2 + n * n // 2 + n * n // 16      # input read twice (amax, quantise), codes, scales
+    gbs = nbytes / (ms_sr * 1e-3) / 1e9
+    return {"us_per_step": round(ms_sr * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "us_per_step_round_to_nearest": round(ms_rn * 1e3, 2),
+            "step": "tensor amax + NVFP4 quantise with stochastic rounding (Philox4x64-10 per element)"}
 
 
 def cpu_baseline_gemm(a, b, K, budget_s=12.0):
@@ -402,6 +422,7 @@ def main():
     b8192 = head.pop("b")
     todo = [("mxfp4_quantize_8192", lambda: mxfp4_quantize_8192(torch, fp4, a8192)),
             ("mxfp4_gemm_requant_8192", lambda: mxfp4_gemm_requant_8192(torch, fp4, synth, a8192, b8192)),
+            ("nvfp4_quantize_sr_8192", lambda: nvfp4_quantize_sr_8192(torch, fp4, synth)),
             ("nvfp4_decode_m1", lambda: nvfp4_decode(torch, fp4, synth, 1)),
             ("nvfp4_decode_m8", lambda: nvfp4_decode(torch, fp4, synth, 8)),
             ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),

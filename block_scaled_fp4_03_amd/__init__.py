@@ -24,7 +24,7 @@ TS_GIVEN = 1
 OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP = 0, 1, 2, 3
 ACT_NONE, ACT_RELU = 0, 1
 
-FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
+FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_sr", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
              "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_status_string")
 
 
@@ -49,6 +49,7 @@ def lib():
             "fp4_scale_bytes": (I64, [I32, I64, I64]),
             "fp4_workspace_size": (SZ, [I32, I32, I64, I64, I64, I32]),
             "fp4_quantize": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P, SZ, P]),
+            "fp4_quantize_sr": (I32, [P, I32, P, P, P, I64, I64, I32, U32, ctypes.c_uint64, P, SZ, P]),
             "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
             "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_ex": (I32, [P, P, P, P, P, P, P, I32, P, P, I64, I64, I64, I32, I32, P]),
@@ -82,6 +83,12 @@ def fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, f
                  stream):
     return lib().fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
                               workspace_bytes, stream)
+
+
+def fp4_quantize_sr(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, seed, workspace,
+                    workspace_bytes, stream):
+    return lib().fp4_quantize_sr(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags,
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, workspace, workspace_bytes, stream)
 
 
 def fp4_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows, K, stream):
@@ -155,11 +162,12 @@ class Quantized:
         self.fmt, self.rows, self.K = fmt, rows, K
 
 
-def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None):
+def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=None):
     """Quantise a 2-D float32/bfloat16 CUDA tensor along its last dimension.
 
     NVFP4: pass `tensor_scale` (a 1-element float32 tensor) to use a given
-    scale; otherwise one is computed and returned in the result."""
+    scale; otherwise one is computed and returned in the result.  sr_seed:
+    round the elements stochastically with that seed (fp4_quantize_sr)."""
     torch = _torch()
     rows, K = x.shape
     dev = x.device
@@ -176,9 +184,14 @@ def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None):
     flags = TS_GIVEN if (fmt == NVFP4 and tensor_scale is not None) else 0
     if fmt == NVFP4 and not flags and ws is None:
         ws = workspace(OP_QUANTIZE, fmt, rows, 0, K, device=dev)
-    rc = fp4_quantize(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
-                      _dtype_code(x), flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
-    _check(rc, "fp4_quantize")
+    if sr_seed is None:
+        rc = fp4_quantize(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
+                          _dtype_code(x), flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    else:
+        rc = fp4_quantize_sr(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
+                             _dtype_code(x), flags, sr_seed, _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream))
+    _check(rc, "fp4_quantize_sr" if sr_seed is not None else "fp4_quantize")
     return out
 
 

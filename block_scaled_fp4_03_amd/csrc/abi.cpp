@@ -48,9 +48,9 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
   }
 }
 
-int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
-                 int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                         int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
+                         size_t workspace_bytes, bool sr, uint64_t seed, void* stream) {
   if (!fmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
   if (flags & ~FP4_TS_GIVEN) return FP4_ERR_FLAGS;
@@ -69,12 +69,27 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
   }
   hipStream_t s = as_stream(stream);
   if (compute_ts && fp4::quantize_nv_small_applies(rows, K, in_dtype))
-    return launched(fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, s));
+    return launched(
+        fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
   if (compute_ts) {
     int rc = launched(fp4::launch_tensor_amax(x, in_dtype, rows * K, static_cast<uint32_t*>(workspace), tensor_scale, s));
     if (rc != FP4_OK) return rc;
   }
-  return launched(fp4::launch_quantize(x, fmt, in_dtype, codes, block_scales, tensor_scale, rows, K, s));
+  return launched(fp4::launch_quantize(x, fmt, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
+}
+
+int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                 int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
+                       workspace_bytes, false, 0ull, stream);
+}
+
+int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                    int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
+                       workspace_bytes, true, seed, stream);
 }
 
 int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt, void* out,

@@ -175,4 +175,73 @@ __device__ __forceinline__ v8h decode8(uint32_t w, v2h s) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// ---- stochastic rounding (NVFP4 video transcript, the training recipe's
+// fourth part: a value between two representable points goes up with
+// probability equal to its distance from the lower one, so the expectation
+// is kept).  Random words: Philox4x64-10 (Salmon, Moraes, Dror, Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011), ten rounds of
+// two 64 x 64 -> 128-bit products mixed with the key, the key advanced by
+// two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// The random words of elements i0 .. i0 + 7 (row-major flat index of the
+// quantised matrix, i0 % 8 == 0) under `seed`: one Philox block with key
+// (seed, 0) and counter (i0 / 8, 0, 0, 0); element i0 + j takes word j / 2,
+// its low 32 bits for even j.
+__device__ __forceinline__ void sr_words8(uint64_t seed, uint64_t i0, uint32_t (&r)[8]) {
+  uint64_t c[4] = {i0 >> 3, 0ull, 0ull, 0ull};
+  philox4x64_10(c, seed, 0ull);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = (uint32_t)c[j];
+    r[2 * j + 1] = (uint32_t)(c[j] >> 32);
+  }
+}
+
+// E2M1 grid value of magnitude code c (0..7).
+__device__ __forceinline__ float e2m1_grid(uint32_t c) {
+  return c < 2u ? 0.5f * (float)c : u2f(((c >> 1) + 126u) << 23) * (1.0f + 0.5f * (float)(c & 1u));
+}
+
+// Stochastically rounded E2M1 code of an already scaled value y (sign bit
+// copied): lo = the largest grid value <= |y| (|y| >= 6 saturates to 6), hi
+// the next one; up iff u * (hi - lo) < |y| - lo with u = (r >> 8) * 2^-24.
+// Every term is exact in FP32 (hi - lo is a power of two, |y| - lo exact), so
+// the decision is exact.
+__device__ __forceinline__ uint32_t e2m1_sr_code(float y, uint32_t r) {
+  const float a = fabsf(y);
+  const uint32_t lo = (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) + (uint32_t)(a >= 2.0f) +
+                      (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f) + (uint32_t)(a >= 6.0f);
+  const float glo = e2m1_grid(lo), ghi = e2m1_grid(lo < 7u ? lo + 1u : 7u);
+  const float u = (float)(r >> 8) * 0x1p-24f;
+  const uint32_t up = (lo < 7u && u * (ghi - glo) < a - glo) ? 1u : 0u;
+  return (lo + up) | ((f2u(y) >> 28) & 8u);
+}
+
+// Eight scaled values to eight stochastically rounded codes (element 2i in
+// the low nibble of byte i).
+__device__ __forceinline__ uint32_t pack8_sr(const float y[8], const uint32_t (&r)[8]) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= e2m1_sr_code(y[k], r[k]) << (4 * k);
+  return w;
+}
+
 }  // namespace fp4

@@ -15,9 +15,12 @@ hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* 
 // (every workgroup reduces the whole maximum itself).
 bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype);
 hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
-                                    float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream);
+                                    float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                    hipStream_t stream);
+// sr: round the elements stochastically (Philox4x64-10 words keyed by seed).
 hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
-                           const float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream);
+                           const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                           hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
                              void* out, int out_dtype, int64_t rows, int64_t K, hipStream_t stream);
 

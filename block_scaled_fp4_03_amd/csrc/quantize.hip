@@ -97,10 +97,13 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
 // each) of one row; waves cover rows_pad = 32 * ceil(rows/32) rows so that the
 // padding rows of the scale tiles are written (as 0).
 // ---------------------------------------------------------------------------
-template <int FMT, int DT>
+// SR: the elements are rounded stochastically (Philox words keyed by seed);
+// the scales are unchanged.
+template <int FMT, int DT, bool SR>
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, uint32_t rows, uint32_t K,
-                                                          uint32_t KT, uint32_t KT2, uint32_t total_waves) {
+                                                          uint32_t KT, uint32_t KT2, uint32_t total_waves,
+                                                          uint64_t seed) {
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
   const uint32_t lane = threadIdx.x & 63u;
   if (wave >= total_waves) return;
@@ -127,7 +130,15 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
     float y[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) y[k] = v[k] * inv;
-    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
+    uint32_t w;
+    if (SR) {
+      uint32_t r[8];
+      sr_words8(seed, (uint64_t)row * K + k0, r);
+      w = pack8_sr(y, r);
+    } else {
+      w = pack8(y);
+    }
+    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = w;
   }
   // Tile t = lane / 32 holds blocks 8t..8t+7 of the slice (block q of the
   // slice in lanes 4q..4q+3).  Its dword for chunk j (lanes 32t + j, j < 2)
@@ -170,9 +181,10 @@ __device__ __forceinline__ bool load_nv_wave(const void* __restrict__ x, uint32_
   return valid;
 }
 
+template <bool SR>
 __device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales, float s_t, uint32_t K, uint32_t KT,
-                                                 uint32_t KT2, uint32_t wave, uint32_t lane) {
+                                                 uint32_t KT2, uint32_t wave, uint32_t lane, uint64_t seed) {
   const uint32_t row = wave / KT2, kt2 = wave % KT2;
   const uint32_t k0 = kt2 * 512u + lane * 8u;
   float am = 0.0f;
@@ -192,7 +204,15 @@ __device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, u
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[k] = nv_div(v[k], d, rd);
     }
-    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = pack8(y);
+    uint32_t w;
+    if (SR) {
+      uint32_t r[8];
+      sr_words8(seed, (uint64_t)row * K + k0, r);
+      w = pack8_sr(y, r);
+    } else {
+      w = pack8(y);
+    }
+    *reinterpret_cast<uint32_t*>(codes + (size_t)row * (K / 2) + k0 / 2) = w;
   }
   // Tile T = lane / 32 holds blocks q = 0..15 of 16 values (block q in lanes
   // 32T + 2q, 32T + 2q + 1).  Tile lane 32j + i (j = chunk parity) holds 8
@@ -211,18 +231,18 @@ __device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, u
   }
 }
 
-template <int DT>
+template <int DT, bool SR>
 __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales,
                                                           const float* __restrict__ tensor_scale, uint32_t rows,
                                                           uint32_t K, uint32_t KT, uint32_t KT2,
-                                                          uint32_t total_waves) {
+                                                          uint32_t total_waves, uint64_t seed) {
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
   if (wave >= total_waves) return;
   const uint32_t lane = threadIdx.x & 63u;
   float v[8];
   const bool valid = load_nv_wave<DT>(x, rows, K, KT2, wave, lane, v);
-  quantize_nv_wave(v, valid, codes, scales, *tensor_scale, K, KT, KT2, wave, lane);
+  quantize_nv_wave<SR>(v, valid, codes, scales, *tensor_scale, K, KT, KT2, wave, lane, seed);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,13 +255,13 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNvSmallMaxBytes = 256u * 1024u;
 
-template <int DT>
+template <int DT, bool SR>
 __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __restrict__ x,
                                                                  uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales,
                                                                  float* __restrict__ tensor_scale, size_t n8,
                                                                  uint32_t rows, uint32_t K, uint32_t KT,
-                                                                 uint32_t KT2, uint32_t total_waves) {
+                                                                 uint32_t KT2, uint32_t total_waves, uint64_t seed) {
   __shared__ float red[16];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
   constexpr uint32_t EB = DT == kDtF32 ? 4u : 2u;
@@ -307,7 +327,7 @@ __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __r
       v[2 * k + 1] = u2f(own[0][k] & 0xFFFF0000u);
     }
   }
-  if (wave < total_waves) quantize_nv_wave(v, valid, codes, scales, s_t, K, KT, KT2, wave, lane);
+  if (wave < total_waves) quantize_nv_wave<SR>(v, valid, codes, scales, s_t, K, KT, KT2, wave, lane, seed);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,8 +399,10 @@ bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype) {
   return rows >= 1 && K >= 16 && bytes <= (int64_t)kNvSmallMaxBytes;
 }
 
-hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
-                                    float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream) {
+namespace {
+template <bool SR>
+void launch_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales, float* tensor_scale, int64_t rows,
+                     int64_t K, uint64_t seed, hipStream_t stream) {
   const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
   const uint32_t rows_pad = (r + 31u) / 32u * 32u;
   const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
@@ -388,46 +410,62 @@ hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes,
   const dim3 grid((waves + 15u) / 16u);
   const size_t n8 = (size_t)rows * (size_t)K / 8u;
   if (in_dtype == kDtF32)
-    quantize_nv_small_kernel<kDtF32><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k, KT,
-                                                                     KT2, waves);
+    quantize_nv_small_kernel<kDtF32, SR><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k,
+                                                                         KT, KT2, waves, seed);
   else
-    quantize_nv_small_kernel<kDtBF16><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k, KT,
-                                                                      KT2, waves);
+    quantize_nv_small_kernel<kDtBF16, SR><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, n8, r, k,
+                                                                          KT, KT2, waves, seed);
+}
+
+template <bool SR>
+void launch_q(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales, const float* tensor_scale,
+              int64_t rows, int64_t K, uint64_t seed, hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
+  const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
+  const uint32_t waves = rows_pad * KT2;
+  const dim3 grid((waves + 3u) / 4u), block(256);
+  const bool f32 = in_dtype == kDtF32;
+  if (fmt == kFmtNV) {
+    if (f32)
+      quantize_nv_kernel<kDtF32, SR><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2, waves,
+                                                                 seed);
+    else
+      quantize_nv_kernel<kDtBF16, SR><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2, waves,
+                                                                  seed);
+  } else if (fmt == kFmtMX) {
+    if (f32)
+      quantize_mx_kernel<kFmtMX, kDtF32, SR><<<grid, block, 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves, seed);
+    else
+      quantize_mx_kernel<kFmtMX, kDtBF16, SR><<<grid, block, 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves, seed);
+  } else {
+    if (f32)
+      quantize_mx_kernel<kFmtMXOcp, kDtF32, SR><<<grid, block, 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves,
+                                                                            seed);
+    else
+      quantize_mx_kernel<kFmtMXOcp, kDtBF16, SR><<<grid, block, 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves,
+                                                                             seed);
+  }
+}
+}  // namespace
+
+hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                    float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                    hipStream_t stream) {
+  if (sr)
+    launch_nv_small<true>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
+  else
+    launch_nv_small<false>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
-                           const float* tensor_scale, int64_t rows, int64_t K, hipStream_t stream) {
-  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
-  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
-  if (fmt == kFmtNV) {
-    const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
-    const uint32_t waves = rows_pad * KT2;
-    const dim3 grid((waves + 3u) / 4u);
-    if (in_dtype == kDtF32)
-      quantize_nv_kernel<kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
-                                                                 waves);
-    else
-      quantize_nv_kernel<kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
-                                                                  waves);
-  } else {
-    const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
-    const uint32_t waves = rows_pad * KT2;
-    const dim3 grid((waves + 3u) / 4u);
-    if (fmt == kFmtMX) {
-      if (in_dtype == kDtF32)
-        quantize_mx_kernel<kFmtMX, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves);
-      else
-        quantize_mx_kernel<kFmtMX, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2, waves);
-    } else {
-      if (in_dtype == kDtF32)
-        quantize_mx_kernel<kFmtMXOcp, kDtF32><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2,
-                                                                              waves);
-      else
-        quantize_mx_kernel<kFmtMXOcp, kDtBF16><<<grid, dim3(256), 0, stream>>>(x, codes, scales, r, k, KT, KT2,
-                                                                               waves);
-    }
-  }
+                           const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                           hipStream_t stream) {
+  if (sr)
+    launch_q<true>(x, fmt, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
+  else
+    launch_q<false>(x, fmt, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
   return hipGetLastError();
 }
 

@@ -139,6 +139,24 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* fp4_quantize with stochastic rounding of the elements (NVFP4 video
+ * transcript, the training recipe's fourth part: a value between two
+ * representable points goes up with probability equal to its distance from
+ * the lower one, so the expectation is kept -- meant for gradients).  The
+ * block and tensor scales are chosen exactly as by fp4_quantize; only the
+ * E2M1 rounding of each scaled value y changes:
+ *   lo = the largest grid value <= |y| (|y| >= 6 gives 6), hi the next one;
+ *   the code is hi iff u * (hi - lo) < |y| - lo, with u = (w >> 8) * 2^-24 and
+ *   w the element's 32-bit random word; the sign bit is copied.
+ * Random words: Philox4x64-10 (Salmon et al., "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011) with key (seed, 0); element i of the matrix
+ * (row-major, i = r * K + k) takes word (i mod 8) / 2 of the block with
+ * counter (i / 8, 0, 0, 0), its low 32 bits for even i.  The result is a
+ * function of (x, seed) alone.  Arguments and errors as fp4_quantize. */
+int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                    int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Dequantise codes + scales (+ NVFP4 tensor scale) to a rows x K matrix of
  * `out_dtype`.  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,
  * times tensor_scale with one FP32 rounding; BF16 output is the round-to-

@@ -66,6 +66,10 @@ def lib():
             "oracle_nvfp4_tensor_scale": (F, [F]),
             "oracle_tensor_amax": (F, [P, I32, I64]),
             "oracle_quantize": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32]),
+            "oracle_quantize_sr": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32, ctypes.c_uint64]),
+            "oracle_philox4x64_10": (None, [P, P, P]),
+            "oracle_sr_word": (ctypes.c_uint32, [ctypes.c_uint64, ctypes.c_uint64]),
+            "oracle_e2m1_sr_mag": (I32, [F, ctypes.c_uint32]),
             "oracle_dequantize": (None, [P, P, P, I32, P, I32, I64, I64]),
             "oracle_gemm": (None, [P, P, P, P, D, D, I64, I64, I64, I32, P, P]),
             "oracle_epilogue": (None, [P, P, I32, I64, I64, P]),
@@ -148,11 +152,12 @@ def scale_offset(fmt, rows, K, r, b):
 
 
 # ---- quantise / dequantise -------------------------------------------------
-def quantize(x, fmt, tensor_scale=None):
+def quantize(x, fmt, tensor_scale=None, sr_seed=None):
     """x: (rows, K) float32, or uint16 holding BF16 bit patterns.
 
     Returns (codes[rows, K//2] u8, scales[tiled] u8, scales_canon[rows, K//bs] u8,
-    tensor_scale float) -- tensor_scale is 1.0 for MXFP4."""
+    tensor_scale float) -- tensor_scale is 1.0 for MXFP4.  sr_seed: round the
+    elements stochastically with that seed (scales unchanged)."""
     x = np.ascontiguousarray(x)
     dt = DT_BF16 if x.dtype == np.uint16 else DT_F32
     if dt == DT_F32:
@@ -163,11 +168,32 @@ def quantize(x, fmt, tensor_scale=None):
     scales = np.zeros(scale_bytes(fmt, rows, K), np.uint8)
     canon = np.zeros((rows, K // bs), np.uint8)
     ts = np.array([1.0 if tensor_scale is None else tensor_scale], np.float32)
-    rc = lib().oracle_quantize(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
-                               int(tensor_scale is not None))
+    if sr_seed is None:
+        rc = lib().oracle_quantize(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
+                                   int(tensor_scale is not None))
+    else:
+        rc = lib().oracle_quantize_sr(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
+                                      int(tensor_scale is not None), int(sr_seed) & 0xFFFFFFFFFFFFFFFF)
     if rc != 0:
         raise ValueError("oracle_quantize: unsupported shape")
     return codes, scales, canon, float(ts[0])
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64-10 block: counter (4 uint64), key (2 uint64) -> 4 uint64."""
+    c = np.array([np.uint64(int(v) & 0xFFFFFFFFFFFFFFFF) for v in counter], dtype=np.uint64)
+    k = np.array([np.uint64(int(v) & 0xFFFFFFFFFFFFFFFF) for v in key], dtype=np.uint64)
+    out = np.zeros(4, np.uint64)
+    lib().oracle_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sr_word(seed, i):
+    return int(lib().oracle_sr_word(int(seed) & 0xFFFFFFFFFFFFFFFF, int(i)))
+
+
+def e2m1_sr_mag(y, r):
+    return int(lib().oracle_e2m1_sr_mag(float(y), int(r) & 0xFFFFFFFF))
 
 
 def dequantize(codes, scales, tensor_scale, fmt, rows, K, out_bf16=False):

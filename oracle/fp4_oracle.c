@@ -263,10 +263,82 @@ float oracle_tensor_amax(const void* x, int dt, int64_t n)
     return m;
 }
 
+/* ------------------------------------------------------------------ */
+/* Stochastic rounding ([P2], the training recipe's fourth part: a value
+ * between two representable points goes up with probability equal to its
+ * distance from the lower point -- 0.3 becomes 1 with probability 30% and
+ * 0 otherwise -- so the expectation is kept).
+ * Random words come from Philox4x64-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), a counter-
+ * based generator: ten rounds, each two 64 x 64 -> 128-bit products of
+ * counter words with the multipliers below, mixed with the key; the key is
+ * advanced by the two Weyl constants between rounds.                     */
+/* ------------------------------------------------------------------ */
+void oracle_philox4x64_10(const uint64_t* ctr, const uint64_t* key, uint64_t* out)
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        unsigned __int128 p0 = (unsigned __int128)M0 * c0;
+        unsigned __int128 p1 = (unsigned __int128)M1 * c2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* The 32-bit random word of element i (row-major flat index of the
+ * quantised matrix) under `seed`: Philox4x64-10 with key (seed, 0) and
+ * counter (i / 8, 0, 0, 0); word (i mod 8) / 2 of the output, its low 32
+ * bits for even i, high 32 bits for odd i.  (Reading: the pages name no
+ * generator; a counter-based one makes the result a function of the seed
+ * and the element alone.) */
+uint32_t oracle_sr_word(uint64_t seed, uint64_t i)
+{
+    uint64_t ctr[4] = {i >> 3, 0, 0, 0}, key[2] = {seed, 0}, out[4];
+    oracle_philox4x64_10(ctr, key, out);
+    uint64_t w = out[(i & 7) >> 1];
+    return (uint32_t)((i & 1) ? (w >> 32) : w);
+}
+
+/* E2M1 magnitude code of y >= 0 rounded stochastically with word r: lo =
+ * the largest grid value <= y (y >= 6 saturates to code 7), hi the next
+ * one; round up iff u * (hi - lo) < y - lo with u = (r >> 8) * 2^-24.
+ * Every quantity is exact in FP32 (hi - lo is a power of two; y - lo is
+ * exact because lo >= hi / 2 or lo = 0), so the decision is too, and
+ * P(up) = ceil((y - lo) / (hi - lo) * 2^24) / 2^24. */
+int oracle_e2m1_sr_mag(float y, uint32_t r)
+{
+    int lo = 0;
+    while (lo < 7 && (float)oracle_e2m1_value(lo + 1) <= y)
+        ++lo;
+    if (lo == 7)
+        return 7;
+    float glo = (float)oracle_e2m1_value(lo), ghi = (float)oracle_e2m1_value(lo + 1);
+    float u = (float)(r >> 8) * 0x1p-24f;
+    return (u * (ghi - glo) < y - glo) ? lo + 1 : lo;
+}
+
 /* Quantise one block of `bs` values.  Writes 4-bit codes (one per byte, in
  * codes_out[0..bs)) and returns the scale byte.  `rule` is the format;
- * s_t is the NVFP4 tensor scale (ignored for MXFP4). */
-static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* codes_out)
+ * s_t is the NVFP4 tensor scale (ignored for MXFP4).  sr: round the
+ * elements stochastically (element k's word: oracle_sr_word(seed, base + k));
+ * the scales are chosen exactly as without it. */
+static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* codes_out, int sr, uint64_t seed,
+                          int64_t base)
 {
     float amax = 0.0f;
     for (int k = 0; k < bs; ++k)
@@ -281,7 +353,9 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
         float d = (float)oracle_e4m3_value(sbyte) * s_t;
         for (int k = 0; k < bs; ++k) {
             int sign = signbit(v[k]) ? 8 : 0;
-            int mag = (sbyte == 0) ? 0 : oracle_e2m1_encode_mag(fabsf(v[k]) / d);
+            float y = (sbyte == 0) ? 0.0f : fabsf(v[k]) / d;
+            int mag = sr ? oracle_e2m1_sr_mag(y, oracle_sr_word(seed, (uint64_t)(base + k)))
+                         : oracle_e2m1_encode_mag(y);
             codes_out[k] = (uint8_t)(sign | mag);
         }
     } else {
@@ -290,7 +364,9 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
         for (int k = 0; k < bs; ++k) {
             int sign = signbit(v[k]) ? 8 : 0;
             float y = ldexpf(fabsf(v[k]), -e);
-            codes_out[k] = (uint8_t)(sign | oracle_e2m1_encode_mag(y));
+            int mag = sr ? oracle_e2m1_sr_mag(y, oracle_sr_word(seed, (uint64_t)(base + k)))
+                         : oracle_e2m1_encode_mag(y);
+            codes_out[k] = (uint8_t)(sign | mag);
         }
     }
     return sbyte;
@@ -304,8 +380,9 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
  *   tensor_scale: NVFP4 only.  If ts_given, *tensor_scale is read;
  *           otherwise it is computed from the whole operand and written.
  * Returns 0, or -1 on a shape the formats do not define. */
-int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
-                    uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given)
+static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
+                           uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given, int sr,
+                           uint64_t seed)
 {
     int bs = (int)block_size(fmt);
     if (rows < 0 || K < 0 || K % bs != 0)
@@ -327,7 +404,7 @@ int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uin
         for (int64_t b = 0; b < KB; ++b) {
             for (int k = 0; k < bs; ++k)
                 v[k] = load_elem(x, dt, r * K + b * bs + k);
-            int sb = quantize_block(v, bs, fmt, s_t, c);
+            int sb = quantize_block(v, bs, fmt, s_t, c, sr, seed, r * K + b * bs);
             scales[oracle_scale_offset(fmt, rows, K, r, b)] = (uint8_t)sb;
             if (scales_canon)
                 scales_canon[r * KB + b] = (uint8_t)sb;
@@ -336,6 +413,20 @@ int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uin
         }
     }
     return 0;
+}
+
+int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
+                    uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given)
+{
+    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 0, 0);
+}
+
+/* As oracle_quantize, with the elements rounded stochastically under `seed`
+ * (scales unchanged). */
+int oracle_quantize_sr(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
+                       uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given, uint64_t seed)
+{
+    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 1, seed);
 }
 
 /* Exact value of element (r, k) of a quantised matrix, without the tensor

@@ -368,3 +368,122 @@ def test_epilogue_rounds_once_to_fp32(orc):
 def test_epilogue_rejects_wrong_bias_length(orc):
     with pytest.raises(ValueError):
         orc.epilogue(np.zeros((2, 3)), np.zeros(2, np.float32))
+
+
+# ---- stochastic rounding (NVFP4 video transcript, the training recipe's
+# fourth part: 0.3 rounds to 1 with probability 30%, to 0 otherwise) --------
+def _u64(v):
+    return np.array([np.uint64(int(x) & 0xFFFFFFFFFFFFFFFF) for x in v], dtype=np.uint64)
+
+
+@pytest.mark.parametrize("counter,key", [([1, 0, 0, 0], [0, 0]), ([6, 0, 0, 0], [7, 0]),
+                                         ([123456789, 2 ** 63 + 5, 77, 2 ** 64 - 1], [2 ** 64 - 3, 99]),
+                                         ([2 ** 40, 3, 2 ** 62, 9], [0x243F6A8885A308D3, 0x13198A2E03707344])])
+def test_philox_matches_numpy(orc, counter, key):
+    """The oracle's Philox4x64-10 equals numpy's Philox bit generator, which
+    advances its counter before each block (so counter - 1 is passed)."""
+    c = _u64(counter)
+    before = c.copy()
+    before[0] -= np.uint64(1)
+    ref = np.random.Philox(counter=before, key=_u64(key)).random_raw(4)
+    np.testing.assert_array_equal(orc.philox4x64_10(c, key), ref)
+
+
+def test_sr_word_layout(orc):
+    seed = 0x0123456789ABCDEF
+    for i in range(24):
+        blk = orc.philox4x64_10([i // 8, 0, 0, 0], [seed, 0])
+        w = int(blk[(i % 8) // 2])
+        assert orc.sr_word(seed, i) == ((w >> 32) if i % 2 else (w & 0xFFFFFFFF))
+
+
+def test_sr_mag_exact_probability(orc):
+    """Round up iff (r >> 8) < f * 2^24 for y = lo + f (hi - lo): on grid points
+    never, above 6 saturate; otherwise exactly ceil(f 2^24) of the 2^24 words."""
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for c, g in enumerate(grid):
+        for r in (0, 1 << 8, 0x80000000, 0xFFFFFFFF):
+            assert orc.e2m1_sr_mag(g, r) == c
+    assert orc.e2m1_sr_mag(6.5, 0) == 7 and orc.e2m1_sr_mag(1e30, 0xFFFFFFFF) == 7
+    for lo in range(7):
+        glo, ghi = grid[lo], grid[lo + 1]
+        for f in (0.25, 0.3, 0.5, 0.75, 2.0 ** -20):
+            y = np.float32(glo + f * (ghi - glo))
+            n = (float(y) - glo) / (ghi - glo) * 2 ** 24          # exact: y - lo and hi - lo are exact
+            k_up = int(np.ceil(n)) - 1                            # largest u index that still rounds up
+            assert orc.e2m1_sr_mag(y, k_up << 8) == lo + 1
+            assert orc.e2m1_sr_mag(y, (k_up + 1) << 8) == lo
+            assert orc.e2m1_sr_mag(y, 0xFF) == lo + 1             # u = 0: up for any y > lo
+
+
+def test_sr_transcript_example(orc):
+    """The transcript's example: 0.3 where the representable neighbours are 0
+    and 1 (an MXFP4 block whose maximum 12 gives scale 2, grid step 1 near 0)
+    becomes 1 in about 30% of the seeds and 0 otherwise; the mean is 0.3."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 12.0
+    x[0, 1:] = 0.3
+    vals = []
+    for seed in range(4000):
+        c, s, _, _ = orc.quantize(x, orc.FMT_MXFP4, sr_seed=seed)
+        v = orc.dequantize(c, s, 1.0, orc.FMT_MXFP4, 1, 32)[0, 1:]
+        assert set(np.unique(v)) <= {0.0, 1.0}
+        vals.append(v)
+    p = np.concatenate(vals).mean()
+    assert abs(p - 0.3) < 4 * np.sqrt(0.3 * 0.7 / (4000 * 31))
+
+
+def _neighbours(orc, x, canon, ts, fmt):
+    """The two grid points bracketing each element, as signed values: MXFP4
+    divisor 2^(byte - 127); NVFP4 divisor E4M3(byte) * s_t (FP32)."""
+    bs = orc.block_size(fmt)
+    if fmt == orc.FMT_NVFP4:
+        e4 = np.array([orc.e4m3_value(int(b)) for b in canon.reshape(-1)], np.float32).reshape(canon.shape)
+        d = (e4 * np.float32(ts)).astype(np.float32)
+    else:
+        d = np.ldexp(np.float32(1), canon.astype(np.int32) - 127).astype(np.float32)
+    d = np.repeat(d, bs, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(d > 0, np.abs(x) / d, 0).astype(np.float32)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    lo_i = np.clip(np.searchsorted(grid, y, side="right") - 1, 0, 7)
+    hi_i = np.minimum(lo_i + 1, 7)
+    hi_i = np.where(grid[lo_i] == y, lo_i, hi_i)
+    sgn = np.where(np.signbit(x), -1.0, 1.0)
+    scale = d.astype(np.float64)
+    return sgn * grid[lo_i] * scale, sgn * grid[hi_i] * scale, sgn * np.minimum(np.abs(x), 6.0 * scale)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_sr_unbiased_and_scales_unchanged(orc, fmt):
+    """Every stochastic value is one of the element's two grid neighbours,
+    the scales equal the deterministic quantiser's, and over n seeds the mean
+    lies within 4 sigma (sigma <= (hi - lo) / (2 sqrt n)) of x -- of x clipped
+    to 6 x divisor where the block scale lets an element saturate (the OCP
+    rule, or an E4M3 block scale rounded down)."""
+    rows, K = 4, 64
+    x = synth.gaussian(61, (rows, K))
+    c0, s0, canon, ts0 = orc.quantize(x, fmt)
+    lo, hi, clipped = _neighbours(orc, x, canon, ts0, fmt)
+    n = 400
+    acc = np.zeros((rows, K))
+    for seed in range(n):
+        c, s, _, ts = orc.quantize(x, fmt, sr_seed=seed * 7919 + 1)
+        np.testing.assert_array_equal(s, s0)
+        assert ts == ts0
+        d = orc.dequantize(c, s, ts, fmt, rows, K).astype(np.float64)
+        tol = np.abs(hi) * 2.0 ** -20 + 1e-30
+        assert (np.minimum(np.abs(d - lo), np.abs(d - hi)) <= tol).all()
+        acc += d
+    mean = acc / n
+    sigma = np.abs(hi - lo) / (2 * np.sqrt(n))
+    assert (np.abs(mean - clipped) <= 4 * sigma + np.abs(clipped) * 2.0 ** -20 + 1e-30).all()
+
+
+def test_sr_reproducible_and_seed_dependent(orc):
+    x = synth.gaussian(62, (8, 128))
+    a = orc.quantize(x, orc.FMT_NVFP4, sr_seed=5)
+    b = orc.quantize(x, orc.FMT_NVFP4, sr_seed=5)
+    c = orc.quantize(x, orc.FMT_NVFP4, sr_seed=6)
+    np.testing.assert_array_equal(a[0], b[0])
+    assert (a[0] != c[0]).any()
