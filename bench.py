@@ -30,6 +30,9 @@ workload, and, under "workloads", the other measured workloads:
                           in the same kernel (fp4_gemm_ex); TFLOP/s.
   nvfp4_quantize_sr_8192  8192x8192 BF16 -> NVFP4 with stochastic rounding
                           (fp4_quantize_sr); GB/s.
+  hadamard16_8192         random Hadamard transform, 8192x8192 BF16; GB/s.
+  nvfp4_quantize_2d_weight 14336x4096 FP32 -> NVFP4 with 16x16 patch scales;
+                          GB/s.
 
 Launch-bound steps (decode, 256^3) are captured once in a HIP graph and
 replayed; every replayed result is checked against the eager one.
@@ -213,6 +216,38 @@ def nvfp4_quantize_sr_8192(torch, fp4, synth):
     return {"us_per_step": round(ms_sr * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "us_per_step_round_to_nearest": round(ms_rn * 1e3, 2),
             "step": "tensor amax + NVFP4 quantise with stochastic rounding (Philox4x64-10 per element)"}
+
+
+def hadamard16_8192(torch, fp4, synth):
+    """Random Hadamard transform of an 8192 x 8192 BF16 tensor on 16-value
+    blocks (fp4_hadamard16), BF16 out; GB/s of input read + output written."""
+    n = 8192
+    x = to_dev(torch, synth.to_bf16_bits(synth.gaussian(82, (n, n))))
+    y = torch.empty_like(x)
+    ms = time_steps(torch, lambda i: fp4.hadamard16(x, seed=i, out=y), 30, 5)
+    nbytes = 2 * n * n * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us_per_step": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "step": "y = (1/4) H16 D x per 16-value block along K, BF16 in and out"}
+
+
+def nvfp4_quantize_2d_weight(torch, fp4, synth):
+    """The MLP weight (14336 x 4096, FP32) to NVFP4 with 16 x 16 patch scales
+    (tensor amax + 2-D quantise), beside the 1 x 16 quantiser."""
+    _, w = synth.nvfp4_mlp()
+    wd = to_dev(torch, w)
+    del w
+    q = fp4.quantize(wd, fp4.NVFP4, two_d=True)
+    ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, wd.shape[0], 0, wd.shape[1])
+    ms2 = time_steps(torch, lambda i: fp4.quantize(wd, fp4.NVFP4, ws=ws, out=q, two_d=True), 20, 3)
+    ms1 = time_steps(torch, lambda i: fp4.quantize(wd, fp4.NVFP4, ws=ws, out=q), 20, 3)
+    n = wd.numel()
+    nbytes = 2 * n * 4 + n // 2 + n // 16
+    gbs = nbytes / (ms2 * 1e-3) / 1e9
+    return {"rows": int(wd.shape[0]), "K": int(wd.shape[1]), "us_per_step": round(ms2 * 1e3, 2),
+            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "us_per_step_1x16": round(ms1 * 1e3, 2),
+            "step": "tensor amax + NVFP4 quantise with one scale per 16 x 16 patch (FP32 in)"}
 
 
 def cpu_baseline_gemm(a, b, K, budget_s=12.0):
@@ -423,6 +458,8 @@ def main():
     todo = [("mxfp4_quantize_8192", lambda: mxfp4_quantize_8192(torch, fp4, a8192)),
             ("mxfp4_gemm_requant_8192", lambda: mxfp4_gemm_requant_8192(torch, fp4, synth, a8192, b8192)),
             ("nvfp4_quantize_sr_8192", lambda: nvfp4_quantize_sr_8192(torch, fp4, synth)),
+            ("hadamard16_8192", lambda: hadamard16_8192(torch, fp4, synth)),
+            ("nvfp4_quantize_2d_weight", lambda: nvfp4_quantize_2d_weight(torch, fp4, synth)),
             ("nvfp4_decode_m1", lambda: nvfp4_decode(torch, fp4, synth, 1)),
             ("nvfp4_decode_m8", lambda: nvfp4_decode(torch, fp4, synth, 8)),
             ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),

@@ -20,11 +20,13 @@ MXFP4, NVFP4, MXFP4_OCP = 0, 1, 2
 F32, BF16 = 0, 1
 OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 TS_GIVEN = 1
+Q_SR, Q_2D = 2, 4
 # enum fp4_out / fp4_act (fp4_gemm_ex)
 OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP = 0, 1, 2, 3
 ACT_NONE, ACT_RELU = 0, 1
 
-FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_sr", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
+FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_sr", "fp4_quantize_ex",
+             "fp4_hadamard16", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
              "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_status_string")
 
 
@@ -50,6 +52,8 @@ def lib():
             "fp4_workspace_size": (SZ, [I32, I32, I64, I64, I64, I32]),
             "fp4_quantize": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P, SZ, P]),
             "fp4_quantize_sr": (I32, [P, I32, P, P, P, I64, I64, I32, U32, ctypes.c_uint64, P, SZ, P]),
+            "fp4_quantize_ex": (I32, [P, I32, P, P, P, I64, I64, I32, U32, ctypes.c_uint64, P, SZ, P]),
+            "fp4_hadamard16": (I32, [P, I32, P, I32, I64, I64, ctypes.c_uint64, P]),
             "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
             "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_ex": (I32, [P, P, P, P, P, P, P, I32, P, P, I64, I64, I64, I32, I32, P]),
@@ -89,6 +93,16 @@ def fp4_quantize_sr(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype
                     workspace_bytes, stream):
     return lib().fp4_quantize_sr(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags,
                                  int(seed) & 0xFFFFFFFFFFFFFFFF, workspace, workspace_bytes, stream)
+
+
+def fp4_quantize_ex(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, seed, workspace,
+                    workspace_bytes, stream):
+    return lib().fp4_quantize_ex(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags,
+                                 int(seed) & 0xFFFFFFFFFFFFFFFF, workspace, workspace_bytes, stream)
+
+
+def fp4_hadamard16(x, in_dtype, y, out_dtype, rows, K, seed, stream):
+    return lib().fp4_hadamard16(x, in_dtype, y, out_dtype, rows, K, int(seed) & 0xFFFFFFFFFFFFFFFF, stream)
 
 
 def fp4_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows, K, stream):
@@ -162,12 +176,13 @@ class Quantized:
         self.fmt, self.rows, self.K = fmt, rows, K
 
 
-def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=None):
+def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=None, two_d=False):
     """Quantise a 2-D float32/bfloat16 CUDA tensor along its last dimension.
 
     NVFP4: pass `tensor_scale` (a 1-element float32 tensor) to use a given
     scale; otherwise one is computed and returned in the result.  sr_seed:
-    round the elements stochastically with that seed (fp4_quantize_sr)."""
+    round the elements stochastically with that seed (fp4_quantize_sr).
+    two_d: NVFP4 scales per 16 x 16 patch (fp4_quantize_ex, FP4_Q_2D)."""
     torch = _torch()
     rows, K = x.shape
     dev = x.device
@@ -184,7 +199,12 @@ def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=
     flags = TS_GIVEN if (fmt == NVFP4 and tensor_scale is not None) else 0
     if fmt == NVFP4 and not flags and ws is None:
         ws = workspace(OP_QUANTIZE, fmt, rows, 0, K, device=dev)
-    if sr_seed is None:
+    if two_d:
+        rc = fp4_quantize_ex(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
+                             _dtype_code(x), flags | Q_2D | (Q_SR if sr_seed is not None else 0),
+                             0 if sr_seed is None else sr_seed, _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream))
+    elif sr_seed is None:
         rc = fp4_quantize(_ptr(x), fmt, _ptr(out.codes), _ptr(out.scales), _ptr(out.tensor_scale), rows, K,
                           _dtype_code(x), flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     else:
@@ -192,6 +212,18 @@ def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=
                              _dtype_code(x), flags, sr_seed, _ptr(ws), 0 if ws is None else ws.numel(),
                              _stream(stream))
     _check(rc, "fp4_quantize_sr" if sr_seed is not None else "fp4_quantize")
+    return out
+
+
+def hadamard16(x, seed, out_dtype=None, out=None, stream=None):
+    """Random Hadamard transform of a 2-D float32/bfloat16 CUDA tensor on
+    16-value blocks along its last dimension (fp4_hadamard16)."""
+    torch = _torch()
+    rows, K = x.shape
+    if out is None:
+        out = torch.empty((rows, K), dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    rc = fp4_hadamard16(_ptr(x), _dtype_code(x), _ptr(out), _dtype_code(out), rows, K, seed, _stream(stream))
+    _check(rc, "fp4_hadamard16")
     return out
 
 

@@ -50,10 +50,12 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
 
 static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                          int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
-                         size_t workspace_bytes, bool sr, uint64_t seed, void* stream) {
+                         size_t workspace_bytes, uint64_t seed, void* stream) {
   if (!fmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
-  if (flags & ~FP4_TS_GIVEN) return FP4_ERR_FLAGS;
+  if (flags & ~(FP4_TS_GIVEN | FP4_Q_SR | FP4_Q_2D)) return FP4_ERR_FLAGS;
+  if ((flags & FP4_Q_2D) && fmt != FP4_NVFP4) return FP4_ERR_FMT;
+  const bool sr = (flags & FP4_Q_SR) != 0u, twod = (flags & FP4_Q_2D) != 0u;
   if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
   if (rows * K > (int64_t(1) << 40)) return FP4_ERR_SHAPE;
   if (rows == 0 || K == 0) return FP4_OK;
@@ -68,28 +70,49 @@ static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_
     if (!aligned(workspace, 4)) return FP4_ERR_ALIGN;
   }
   hipStream_t s = as_stream(stream);
-  if (compute_ts && fp4::quantize_nv_small_applies(rows, K, in_dtype))
+  if (compute_ts && !twod && fp4::quantize_nv_small_applies(rows, K, in_dtype))
     return launched(
         fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
   if (compute_ts) {
     int rc = launched(fp4::launch_tensor_amax(x, in_dtype, rows * K, static_cast<uint32_t*>(workspace), tensor_scale, s));
     if (rc != FP4_OK) return rc;
   }
+  if (twod)
+    return launched(fp4::launch_quantize_nv2d(x, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
   return launched(fp4::launch_quantize(x, fmt, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
 }
 
 int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace, size_t workspace_bytes,
                  void* stream) {
+  if (flags & ~FP4_TS_GIVEN) return FP4_ERR_FLAGS;
   return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
-                       workspace_bytes, false, 0ull, stream);
+                       workspace_bytes, 0ull, stream);
 }
 
 int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                     int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
                     size_t workspace_bytes, void* stream) {
+  if (flags & ~FP4_TS_GIVEN) return FP4_ERR_FLAGS;
+  return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags | FP4_Q_SR, workspace,
+                       workspace_bytes, seed, stream);
+}
+
+int fp4_quantize_ex(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                    int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
-                       workspace_bytes, true, seed, stream);
+                       workspace_bytes, seed, stream);
+}
+
+int fp4_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t rows, int64_t K, uint64_t seed,
+                   void* stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
+  if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % 16 != 0) return FP4_ERR_SHAPE;
+  if (rows == 0 || K == 0) return FP4_OK;
+  if (!x || !y) return FP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FP4_ERR_ALIGN;
+  return launched(fp4::launch_hadamard16(x, in_dtype, y, out_dtype, rows, K, seed, as_stream(stream)));
 }
 
 int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt, void* out,

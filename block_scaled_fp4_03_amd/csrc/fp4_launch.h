@@ -17,6 +17,13 @@ bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype);
 hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
                                     float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
                                     hipStream_t stream);
+// NVFP4 with 16 x 16 patch scales (tensor scale already in *tensor_scale).
+hipError_t launch_quantize_nv2d(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                hipStream_t stream);
+// y = random Hadamard transform of x on 16-value blocks along K.
+hipError_t launch_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t rows, int64_t K,
+                             uint64_t seed, hipStream_t stream);
 // sr: round the elements stochastically (Philox4x64-10 words keyed by seed).
 hipError_t launch_quantize(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* scales,
                            const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,

@@ -181,16 +181,19 @@ __device__ __forceinline__ bool load_nv_wave(const void* __restrict__ x, uint32_
   return valid;
 }
 
+// am_in >= 0: the block maximum to use (2-D scaling: the 16 x 16 patch's).
 template <bool SR>
 __device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales, float s_t, uint32_t K, uint32_t KT,
-                                                 uint32_t KT2, uint32_t wave, uint32_t lane, uint64_t seed) {
+                                                 uint32_t KT2, uint32_t wave, uint32_t lane, uint64_t seed,
+                                                 float am_in = -1.0f) {
   const uint32_t row = wave / KT2, kt2 = wave % KT2;
   const uint32_t k0 = kt2 * 512u + lane * 8u;
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
   am = fmaxf(am, __shfl_xor(am, 1));
+  if (am_in >= 0.0f) am = am_in;
   const float r = (am / 6.0f) / s_t;
   const uint32_t sb = e4m3_encode(r);
   if (valid) {
@@ -331,6 +334,108 @@ __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __r
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4 with 2-D block scaling (NVFP4 video transcript, the training recipe's
+// second part: a weight matrix serves as W forward and W^T backward, so its
+// scales are shared by 16 x 16 patches and both directions quantise alike).
+// A workgroup of 16 waves takes 16 rows of one 512-column slice; each wave
+// reduces its row's 16-value block maxima, the 16 rows' maxima meet in LDS,
+// and every row (inside the matrix) quantises with its patch maximum.  Rows
+// past the matrix keep scale byte 0.
+// ---------------------------------------------------------------------------
+template <int DT, bool SR>
+__global__ __launch_bounds__(1024) void quantize_nv2d_kernel(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ tensor_scale, uint32_t rows,
+                                                             uint32_t K, uint32_t KT, uint32_t KT2, uint64_t seed) {
+  __shared__ float blk[16][32];
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  const uint32_t row = blockIdx.y * 16u + w, kt2 = blockIdx.x;
+  const uint32_t wave = row * KT2 + kt2;      // the 1-D kernel's wave index of (row, slice)
+  float v[8];
+  const bool valid = load_nv_wave<DT>(x, rows, K, KT2, wave, lane, v);
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  if ((lane & 1u) == 0u) blk[w][lane >> 1] = am;
+  __syncthreads();
+  float pm = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pm = fmaxf(pm, blk[r][lane >> 1]);
+  quantize_nv_wave<SR>(v, valid, codes, scales, *tensor_scale, K, KT, KT2, wave, lane, seed, row < rows ? pm : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Random Hadamard transform on 16-value blocks along K (NVFP4 video
+// transcript, the training recipe's third part: the block's values are mixed
+// so that an outlier no longer sets its scale alone; the transform is
+// orthogonal, so norms and dot products along K are kept).  y = (1/4) H16 D x
+// per block: D = the signs of column k (top bit of its Philox word under
+// seed, so two matrices transformed with one seed keep their products), H16
+// applied as butterflies of distance 1, 2, 4 (within the lane's 8 values)
+// and 8 (with the neighbouring lane), the 1/4 exact.  A lane holds 8 columns
+// and walks rows; its signs are computed once.
+// ---------------------------------------------------------------------------
+template <int DT, int OT>
+__global__ __launch_bounds__(256) void hadamard16_kernel(const void* __restrict__ x, void* __restrict__ y,
+                                                         uint32_t rows, uint32_t K, uint64_t seed) {
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  const uint32_t k0 = blockIdx.x * 512u + lane * 8u;
+  const bool col_ok = k0 < K;
+  uint32_t r8[8];
+  sr_words8(seed, k0, r8);
+  for (uint32_t row = blockIdx.y * 4u + w; row < rows; row += gridDim.y * 4u) {
+    float v[8];
+    if (col_ok) {
+      load8v<DT>(x, (size_t)row * K + k0, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (r8[k] >> 31) ? -v[k] : v[k];
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2 * h)
+#pragma unroll
+        for (int m = i; m < i + h; ++m) {
+          const float a = v[m], c = v[m + h];
+          v[m] = a + c;
+          v[m + h] = a - c;
+        }
+    // distance 8: positions m (even lane) and m + 8 (odd lane)
+    const bool upper = (lane & 1u) != 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float o = __shfl_xor(v[k], 1);
+      v[k] = upper ? o - v[k] : v[k] + o;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] *= 0.25f;
+    if (col_ok) {
+      if (OT == kDtF32) {
+        u32x4 a, b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[k] = f2u(v[k]);
+          b[k] = f2u(v[4 + k]);
+        }
+        u32x4* p = reinterpret_cast<u32x4*>(static_cast<float*>(y) + (size_t)row * K + k0);
+        p[0] = a;
+        p[1] = b;
+      } else {
+        u32x4 a;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          a[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + (size_t)row * K + k0) = a;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Dequantisation: one lane per 8 elements.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -456,6 +561,54 @@ hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes,
     launch_nv_small<true>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
   else
     launch_nv_small<false>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nv2d(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
+  const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
+  const dim3 grid(KT2, rows_pad / 16u), block(1024);
+  const bool f32 = in_dtype == kDtF32;
+  if (sr) {
+    if (f32)
+      quantize_nv2d_kernel<kDtF32, true><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                      seed);
+    else
+      quantize_nv2d_kernel<kDtBF16, true><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                       seed);
+  } else {
+    if (f32)
+      quantize_nv2d_kernel<kDtF32, false><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                       seed);
+    else
+      quantize_nv2d_kernel<kDtBF16, false><<<grid, block, 0, stream>>>(x, codes, scales, tensor_scale, r, k, KT, KT2,
+                                                                        seed);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t rows, int64_t K,
+                             uint64_t seed, hipStream_t stream) {
+  const uint32_t gx = (uint32_t)((K + 511) / 512);
+  uint32_t gy = (uint32_t)((rows + 3) / 4);
+  const uint32_t cap = gx >= 4096u ? 1u : 4096u / gx;
+  if (gy > cap) gy = cap;
+  const dim3 grid(gx, gy), block(256);
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  if (in_dtype == kDtF32) {
+    if (out_dtype == kDtF32)
+      hadamard16_kernel<kDtF32, kDtF32><<<grid, block, 0, stream>>>(x, y, r, k, seed);
+    else
+      hadamard16_kernel<kDtF32, kDtBF16><<<grid, block, 0, stream>>>(x, y, r, k, seed);
+  } else {
+    if (out_dtype == kDtF32)
+      hadamard16_kernel<kDtBF16, kDtF32><<<grid, block, 0, stream>>>(x, y, r, k, seed);
+    else
+      hadamard16_kernel<kDtBF16, kDtBF16><<<grid, block, 0, stream>>>(x, y, r, k, seed);
+  }
   return hipGetLastError();
 }
 

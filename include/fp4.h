@@ -86,6 +86,9 @@ enum fp4_act { FP4_ACT_NONE = 0, FP4_ACT_RELU = 1 };
 
 /* Flags for fp4_quantize. */
 #define FP4_TS_GIVEN 1u /* NVFP4: read the tensor scale from *tensor_scale instead of computing it */
+/* More flags for fp4_quantize_ex. */
+#define FP4_Q_SR 2u     /* round the elements stochastically (as fp4_quantize_sr)          */
+#define FP4_Q_2D 4u     /* NVFP4 only: one block scale per 16 x 16 patch (2-D scaling)      */
 
 enum fp4_status {
     FP4_OK = 0,
@@ -156,6 +159,42 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
 int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                     int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* fp4_quantize with options (flags may combine):
+ *   FP4_TS_GIVEN: as in fp4_quantize.
+ *   FP4_Q_SR: stochastic rounding of the elements with `seed`, exactly as
+ *     fp4_quantize_sr.
+ *   FP4_Q_2D (NVFP4 only, else FP4_ERR_FMT): 2-D block scaling (NVFP4 video
+ *     transcript, the training recipe's second part: a weight matrix is used
+ *     as W forward and as W^T backward, so one scale serves a 16 x 16 patch
+ *     and both directions quantise alike).  The patch of rows 16p..16p+15
+ *     (those inside the matrix) and columns 16b..16b+15 takes the E4M3 scale
+ *     of its largest magnitude, written for each of its rows in the usual
+ *     layout; rows past the matrix keep scale byte 0.  W and W^T then
+ *     dequantise to exact transposes of each other (rows and K multiples of
+ *     16).  The tensor scale is the usual one.
+ * seed is ignored without FP4_Q_SR.  Arguments and errors otherwise as
+ * fp4_quantize. */
+int fp4_quantize_ex(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                    int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Random Hadamard transform (NVFP4 video transcript, the training recipe's
+ * third part: values are mixed within a block so that an outlier no longer
+ * sets the block scale alone; the transform is orthogonal, so norms and dot
+ * products survive).  On every 16-value block along K of the rows x K matrix
+ * x: y = (1/4) H16 D x, where D holds the signs of the columns (-1 where the
+ * top bit of column k's Philox4x64-10 word under `seed` -- the word
+ * fp4_quantize_sr gives element k of a one-row matrix -- is set), and H16 is
+ * the 16-point Walsh-Hadamard matrix evaluated as FP32 butterflies
+ * (a + b, a - b) of distance 1, 2, 4, 8 in that order; the 1/4 is exact.
+ * Two matrices transformed with one seed keep their products along K, so
+ * transforming both GEMM operands leaves the product unchanged up to
+ * rounding.  x: FP32 or BF16 (in_dtype); y: FP32 or BF16 (out_dtype, round to
+ * nearest even), may equal x when the dtypes agree.  K % 16 == 0; x and y
+ * 16-byte aligned.  rows == 0 or K == 0 is a no-op. */
+int fp4_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t rows, int64_t K, uint64_t seed,
+                   void* stream);
 
 /* Dequantise codes + scales (+ NVFP4 tensor scale) to a rows x K matrix of
  * `out_dtype`.  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,

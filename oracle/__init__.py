@@ -68,6 +68,8 @@ def lib():
             "oracle_quantize": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32]),
             "oracle_quantize_sr": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32, ctypes.c_uint64]),
             "oracle_philox4x64_10": (None, [P, P, P]),
+            "oracle_quantize_ex": (I32, [P, I32, I32, I64, I64, P, P, P, P, I32, I32, ctypes.c_uint64, I32]),
+            "oracle_rht16": (None, [P, I32, I64, I64, ctypes.c_uint64, P]),
             "oracle_sr_word": (ctypes.c_uint32, [ctypes.c_uint64, ctypes.c_uint64]),
             "oracle_e2m1_sr_mag": (I32, [F, ctypes.c_uint32]),
             "oracle_dequantize": (None, [P, P, P, I32, P, I32, I64, I64]),
@@ -152,12 +154,13 @@ def scale_offset(fmt, rows, K, r, b):
 
 
 # ---- quantise / dequantise -------------------------------------------------
-def quantize(x, fmt, tensor_scale=None, sr_seed=None):
+def quantize(x, fmt, tensor_scale=None, sr_seed=None, two_d=False):
     """x: (rows, K) float32, or uint16 holding BF16 bit patterns.
 
     Returns (codes[rows, K//2] u8, scales[tiled] u8, scales_canon[rows, K//bs] u8,
     tensor_scale float) -- tensor_scale is 1.0 for MXFP4.  sr_seed: round the
-    elements stochastically with that seed (scales unchanged)."""
+    elements stochastically with that seed (scales unchanged).  two_d: NVFP4
+    block scales shared by 16 x 16 patches."""
     x = np.ascontiguousarray(x)
     dt = DT_BF16 if x.dtype == np.uint16 else DT_F32
     if dt == DT_F32:
@@ -168,12 +171,13 @@ def quantize(x, fmt, tensor_scale=None, sr_seed=None):
     scales = np.zeros(scale_bytes(fmt, rows, K), np.uint8)
     canon = np.zeros((rows, K // bs), np.uint8)
     ts = np.array([1.0 if tensor_scale is None else tensor_scale], np.float32)
-    if sr_seed is None:
+    if sr_seed is None and not two_d:
         rc = lib().oracle_quantize(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
                                    int(tensor_scale is not None))
     else:
-        rc = lib().oracle_quantize_sr(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
-                                      int(tensor_scale is not None), int(sr_seed) & 0xFFFFFFFFFFFFFFFF)
+        rc = lib().oracle_quantize_ex(_p(x), dt, fmt, rows, K, _p(codes), _p(scales), _p(canon), _p(ts),
+                                      int(tensor_scale is not None), int(sr_seed is not None),
+                                      0 if sr_seed is None else int(sr_seed) & 0xFFFFFFFFFFFFFFFF, int(bool(two_d)))
     if rc != 0:
         raise ValueError("oracle_quantize: unsupported shape")
     return codes, scales, canon, float(ts[0])
@@ -186,6 +190,20 @@ def philox4x64_10(counter, key):
     out = np.zeros(4, np.uint64)
     lib().oracle_philox4x64_10(_p(c), _p(k), _p(out))
     return out
+
+
+def rht16(x, seed):
+    """Random Hadamard transform on 16-value blocks along K (float32 out)."""
+    x = np.ascontiguousarray(x)
+    dt = DT_BF16 if x.dtype == np.uint16 else DT_F32
+    if dt == DT_F32:
+        x = x.astype(np.float32, copy=False)
+    rows, K = x.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    y = np.empty((rows, K), np.float32)
+    lib().oracle_rht16(_p(x), dt, rows, K, int(seed) & 0xFFFFFFFFFFFFFFFF, _p(y))
+    return y
 
 
 def sr_word(seed, i):

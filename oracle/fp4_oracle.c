@@ -338,11 +338,13 @@ int oracle_e2m1_sr_mag(float y, uint32_t r)
  * elements stochastically (element k's word: oracle_sr_word(seed, base + k));
  * the scales are chosen exactly as without it. */
 static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* codes_out, int sr, uint64_t seed,
-                          int64_t base)
+                          int64_t base, float amax_in)
 {
     float amax = 0.0f;
     for (int k = 0; k < bs; ++k)
         if (fabsf(v[k]) > amax) amax = fabsf(v[k]);
+    if (amax_in >= 0.0f)
+        amax = amax_in;   /* 2-D scaling: the 16 x 16 patch's maximum */
 
     int sbyte;
     if (rule == OR_FMT_NVFP4) {
@@ -380,12 +382,21 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
  *   tensor_scale: NVFP4 only.  If ts_given, *tensor_scale is read;
  *           otherwise it is computed from the whole operand and written.
  * Returns 0, or -1 on a shape the formats do not define. */
+/* 2-D block scaling ([P2], the training recipe's second part: a weight
+ * matrix is used as W in the forward pass and as W^T in the backward pass,
+ * so NVFP4 scales are shared by 16 x 16 patches instead of 1 x 16 blocks;
+ * W and W^T then quantise alike).  Reading: the patch of rows 16p..16p+15
+ * (those inside the matrix) and columns 16b..16b+15 takes the E4M3 scale of
+ * its largest magnitude, and every row of it uses that scale; rows past the
+ * matrix keep scale byte 0 as in the 1-D layout.                          */
 static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
                            uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given, int sr,
-                           uint64_t seed)
+                           uint64_t seed, int twod)
 {
     int bs = (int)block_size(fmt);
     if (rows < 0 || K < 0 || K % bs != 0)
+        return -1;
+    if (twod && fmt != OR_FMT_NVFP4)
         return -1;
     float s_t = 1.0f;
     if (fmt == OR_FMT_NVFP4) {
@@ -404,7 +415,17 @@ static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t
         for (int64_t b = 0; b < KB; ++b) {
             for (int k = 0; k < bs; ++k)
                 v[k] = load_elem(x, dt, r * K + b * bs + k);
-            int sb = quantize_block(v, bs, fmt, s_t, c, sr, seed, r * K + b * bs);
+            float pm = -1.0f;
+            if (twod) {
+                pm = 0.0f;
+                int64_t r0 = r - r % 16, r1 = r0 + 16 < rows ? r0 + 16 : rows;
+                for (int64_t rr = r0; rr < r1; ++rr)
+                    for (int k = 0; k < bs; ++k) {
+                        float a = fabsf(load_elem(x, dt, rr * K + b * bs + k));
+                        if (a > pm) pm = a;
+                    }
+            }
+            int sb = quantize_block(v, bs, fmt, s_t, c, sr, seed, r * K + b * bs, pm);
             scales[oracle_scale_offset(fmt, rows, K, r, b)] = (uint8_t)sb;
             if (scales_canon)
                 scales_canon[r * KB + b] = (uint8_t)sb;
@@ -418,7 +439,7 @@ static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t
 int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
                     uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given)
 {
-    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 0, 0);
+    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 0, 0, 0);
 }
 
 /* As oracle_quantize, with the elements rounded stochastically under `seed`
@@ -426,7 +447,49 @@ int oracle_quantize(const void* x, int dt, int fmt, int64_t rows, int64_t K, uin
 int oracle_quantize_sr(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes,
                        uint8_t* scales, uint8_t* scales_canon, float* tensor_scale, int ts_given, uint64_t seed)
 {
-    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 1, seed);
+    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, 1, seed, 0);
+}
+
+/* Both options: sr (stochastic rounding under seed) and twod (NVFP4 16 x 16
+ * patch scales). */
+int oracle_quantize_ex(const void* x, int dt, int fmt, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       uint8_t* scales_canon, float* tensor_scale, int ts_given, int sr, uint64_t seed, int twod)
+{
+    return quantize_matrix(x, dt, fmt, rows, K, codes, scales, scales_canon, tensor_scale, ts_given, sr, seed, twod);
+}
+
+/* ------------------------------------------------------------------ */
+/* Random Hadamard transform ([P2], the training recipe's third part: the
+ * values of a block are mixed so that an outlier no longer sets the block
+ * scale alone; the vector's magnitude is unchanged and dot products
+ * survive because the transform is orthogonal).  Reading: on every
+ * 16-value block along K (the NVFP4 block), y = (1/4) H16 D x, with D the
+ * diagonal of signs s_k = -1 if the top bit of oracle_sr_word(seed, k) is
+ * set, else +1 (k = column, so two matrices transformed with one seed keep
+ * their products along K), and H16 the 16-point Walsh-Hadamard matrix
+ * applied as butterflies of distance 1, 2, 4, 8 (a + b, a - b) in FP32,
+ * in that order; the 1/4 is exact.  Output FP32.                        */
+/* ------------------------------------------------------------------ */
+void oracle_rht16(const void* x, int dt, int64_t rows, int64_t K, uint64_t seed, float* y)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / 16; ++b) {
+            float v[16];
+            for (int k = 0; k < 16; ++k) {
+                int64_t col = b * 16 + k;
+                float s = (oracle_sr_word(seed, (uint64_t)col) >> 31) ? -1.0f : 1.0f;
+                v[k] = load_elem(x, dt, r * K + col) * s;
+            }
+            for (int h = 1; h < 16; h *= 2)
+                for (int i = 0; i < 16; i += 2 * h)
+                    for (int m = i; m < i + h; ++m) {
+                        float a = v[m], c = v[m + h];
+                        v[m] = a + c;
+                        v[m + h] = a - c;
+                    }
+            for (int k = 0; k < 16; ++k)
+                y[r * K + b * 16 + k] = v[k] * 0.25f;
+        }
 }
 
 /* Exact value of element (r, k) of a quantised matrix, without the tensor

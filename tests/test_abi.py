@@ -205,3 +205,17 @@ def test_gemm_ex_argument_errors(L):
     assert call(C=FAKE + 4) == -3       # FP4 output codes 16-byte aligned
     assert call(Cs=FAKE + 2) == -3
     assert call(A=FAKE + 8) == -3
+
+
+def test_quantize_ex_and_hadamard_argument_errors(L):
+    q = fp4.fp4_quantize_ex
+    assert q(FAKE, 0, FAKE, FAKE, None, 4, 64, 0, fp4.Q_2D, 0, None, 0, None) == -4     # 2-D needs NVFP4
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 16, 0, None, 0, None) == -8           # unknown flag
+    assert fp4.fp4_quantize(FAKE, 0, FAKE, FAKE, None, 4, 64, 0, fp4.Q_SR, None, 0, None) == -8  # not a quantize flag
+    h = fp4.fp4_hadamard16
+    assert h(FAKE, 0, FAKE, 0, 4, 40, 0, None) == -2       # K % 16
+    assert h(FAKE, 2, FAKE, 0, 4, 64, 0, None) == -5
+    assert h(FAKE, 0, FAKE, 3, 4, 64, 0, None) == -5
+    assert h(None, 0, FAKE, 0, 4, 64, 0, None) == -1
+    assert h(FAKE + 8, 0, FAKE, 0, 4, 64, 0, None) == -3
+    assert h(FAKE, 0, FAKE, 0, 0, 64, 0, None) == 0

@@ -487,3 +487,78 @@ def test_sr_reproducible_and_seed_dependent(orc):
     c = orc.quantize(x, orc.FMT_NVFP4, sr_seed=6)
     np.testing.assert_array_equal(a[0], b[0])
     assert (a[0] != c[0]).any()
+
+
+# ---- random Hadamard transform and 2-D weight scaling (NVFP4 video
+# transcript, the training recipe's third and second parts) ----------------
+def test_rht_equals_hadamard_matrix_times_signs(orc):
+    """On integer inputs every butterfly sum is exact, so the oracle's FP32
+    transform equals (1/4) H16 D x computed with scipy's Hadamard matrix, bit
+    for bit; D holds the signs of the columns' Philox words."""
+    from scipy.linalg import hadamard
+    seed = 424242
+    g = synth.rng(90)
+    x = g.integers(-50, 50, (5, 64)).astype(np.float32)
+    y = orc.rht16(x, seed)
+    H = hadamard(16).astype(np.float64)
+    d = np.array([-1.0 if orc.sr_word(seed, k) >> 31 else 1.0 for k in range(64)])
+    ref = np.concatenate([(0.25 * (H @ (d[16 * b:16 * b + 16] * x[:, 16 * b:16 * b + 16]).T)).T
+                          for b in range(4)], axis=1)
+    np.testing.assert_array_equal(y, ref.astype(np.float32))
+    assert (d > 0).any() and (d < 0).any()
+
+
+def test_rht_keeps_norms_and_dot_products(orc):
+    a = synth.gaussian(91, (4, 256))
+    b = synth.gaussian(92, (6, 256))
+    ta, tb = orc.rht16(a, 7), orc.rht16(b, 7)
+    np.testing.assert_allclose((ta.astype(np.float64) ** 2).sum(1), (a.astype(np.float64) ** 2).sum(1), rtol=1e-6)
+    np.testing.assert_allclose(ta.astype(np.float64) @ tb.T.astype(np.float64),
+                               a.astype(np.float64) @ b.T.astype(np.float64), rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_rht_lowers_quantisation_error_with_outliers(orc, fmt):
+    """The transcript's point: with one large value per block the block scale
+    is set by the outlier; after the transform the error (same norm in both
+    domains, the transform being orthogonal) is smaller.  Holds for MXFP4's
+    32-value power-of-two blocks; NVFP4's 16-value E4M3 blocks already place a
+    lone outlier well, and there the transform raised the error on every
+    outlier density tried (1.1-2.1x)."""
+    x = synth.gaussian(93, (64, 512))
+    x[:, ::16] *= np.float32(30.0)
+    y = orc.rht16(x, 3)
+
+    def err(v):
+        c, s, _, ts = orc.quantize(v, fmt)
+        return float(((orc.dequantize(c, s, ts, fmt, *v.shape).astype(np.float64) - v) ** 2).sum())
+
+    assert err(y) < 0.7 * err(x)
+
+
+def test_2d_scales_make_w_and_wt_quantise_alike(orc):
+    """2-D scaling: W and W^T dequantise to transposes of each other exactly
+    (same 16 x 16 patches, same tensor scale); with 1 x 16 blocks they do not."""
+    w = synth.gaussian(94, (48, 64), std=0.02, bernoulli=0.01)
+    wt = np.ascontiguousarray(w.T)
+    c, s, _, ts = orc.quantize(w, orc.FMT_NVFP4, two_d=True)
+    ct, st, _, tst = orc.quantize(wt, orc.FMT_NVFP4, two_d=True)
+    assert ts == tst
+    d = orc.dequantize(c, s, ts, orc.FMT_NVFP4, 48, 64)
+    dt = orc.dequantize(ct, st, tst, orc.FMT_NVFP4, 64, 48)
+    np.testing.assert_array_equal(d, dt.T)
+    c1, s1, _, _ = orc.quantize(w, orc.FMT_NVFP4)
+    c1t, s1t, _, _ = orc.quantize(wt, orc.FMT_NVFP4)
+    assert not np.array_equal(orc.dequantize(c1, s1, ts, orc.FMT_NVFP4, 48, 64),
+                              orc.dequantize(c1t, s1t, ts, orc.FMT_NVFP4, 64, 48).T)
+
+
+def test_2d_patch_rows_share_scales(orc):
+    w = synth.gaussian(95, (40, 96))          # 40 rows: patch groups of 16, 16 and 8 rows
+    _, _, canon, _ = orc.quantize(w, orc.FMT_NVFP4, two_d=True)
+    for r0 in (0, 16, 32):
+        grp = canon[r0:min(r0 + 16, 40)]
+        assert (grp == grp[0]).all()
+    # the patch scale is the 1-D scale of the patch's largest block
+    _, _, canon1, _ = orc.quantize(w, orc.FMT_NVFP4)
+    np.testing.assert_array_equal(canon[32], canon1[32:40].max(axis=0))
