@@ -53,16 +53,40 @@ __device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
 // the last workgroup to finish turns the maximum into s_t = amax / (6 * 448),
 // writes it, and clears the two workspace words for the next call.
 // ---------------------------------------------------------------------------
+// Each workgroup pass covers a 16 KB span: every lane issues four 16-byte
+// loads (a wave's load reads 1 KB contiguous) before it folds any of them, so
+// that 4 KB per wave are in flight; buffer loads bound the last, partial span
+// without a branch.  The max runs on the magnitude bits (for finite values
+// the integer order is the order of |x|).  A dword holds one FP32 value or
+// two BF16 values (each the high half of an FP32 value).
+constexpr uint32_t kAmaxSpan = 16384u;
+
 template <int DT>
-__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, size_t n8,
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, size_t nbytes,
                                                           uint32_t* __restrict__ ws, float* __restrict__ ts) {
-  float m = 0.0f;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    float v[8];
-    load8v<DT>(x, i * 8, v);
+  uint32_t mb = 0u;
+  const size_t step = (size_t)gridDim.x * kAmaxSpan;
+  for (size_t off = (size_t)blockIdx.x * kAmaxSpan; off < nbytes; off += step) {
+    const size_t rem = nbytes - off;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(static_cast<const uint8_t*>(x) + off, rem < kAmaxSpan ? (uint32_t)rem : kAmaxSpan);
+    u32x4 w[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+    for (uint32_t u = 0; u < 4u; ++u)
+      w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256u + threadIdx.x) * 16u, 0, 0));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (DT == kDtF32) {
+          mb = max(mb, w[u][k] & 0x7FFFFFFFu);
+        } else {
+          mb = max(mb, (w[u][k] << 16) & 0x7FFF0000u);
+          mb = max(mb, w[u][k] & 0x7FFF0000u);
+        }
+      }
   }
+  float m = u2f(mb);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float red[4];
@@ -488,14 +512,14 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* ws, float* tensor_scale,
                               hipStream_t stream) {
-  const size_t n8 = (size_t)n / 8;
-  size_t blocks = (n8 + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  const size_t nbytes = (size_t)n * (in_dtype == kDtF32 ? 4u : 2u);
+  size_t blocks = (nbytes + kAmaxSpan - 1) / kAmaxSpan;
+  if (blocks > 2048) blocks = 2048;   // 8 workgroups of 4 waves per compute unit
   if (blocks < 1) blocks = 1;
   if (in_dtype == kDtF32)
-    tensor_amax_kernel<kDtF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
+    tensor_amax_kernel<kDtF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
   else
-    tensor_amax_kernel<kDtBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, n8, ws, tensor_scale);
+    tensor_amax_kernel<kDtBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
   return hipGetLastError();
 }
 
