@@ -33,6 +33,11 @@ workload, and, under "workloads", the other measured workloads:
   hadamard16_8192         random Hadamard transform, 8192x8192 BF16; GB/s.
   nvfp4_quantize_2d_weight 14336x4096 FP32 -> NVFP4 with 16x16 patch scales;
                           GB/s.
+  w4a8_gemm_8192          the headline's inputs with A quantised to MXFP8
+                          (E4M3) instead: MXFP8 x MXFP4 GEMM (fp4_gemm_w4a8),
+                          BF16 out; TFLOP/s vs the 5.0 PFLOP/s FP8 peak (the
+                          matrix core runs FP8 x FP4 at the FP8 rate).
+  mxfp8_quantize_8192     8192x8192 FP32 -> MXFP8; GB/s.
 
 Launch-bound steps (decode, 256^3) are captured once in a HIP graph and
 replayed; every replayed result is checked against the eager one.
@@ -51,6 +56,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 / FP6 matrix peak
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense FP16 / BF16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROTATE = 8
 METRIC = "FP4 GEMM TFLOPS & % MXFP4 MFMA peak; decode-shape HBM GB/s & % peak"
@@ -248,6 +254,34 @@ def nvfp4_quantize_2d_weight(torch, fp4, synth):
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "us_per_step_1x16": round(ms1 * 1e3, 2),
             "step": "tensor amax + NVFP4 quantise with one scale per 16 x 16 patch (FP32 in)"}
+
+
+def w4a8_gemm_8192(torch, fp4, synth, a, b):
+    """8192^3 W4A8: the headline's A quantised to MXFP8 (E4M3 elements, E8M0
+    32-blocks), its B to MXFP4; 8 rotating operand copies; BF16 out."""
+    n = 8192
+    qa0 = fp4.quantize(to_dev(torch, a), fp4.MXFP8)
+    qb0 = fp4.quantize(to_dev(torch, b), fp4.MXFP4)
+    qa = [qa0] + [fp4.Quantized(qa0.codes.clone(), qa0.scales.clone(), None, fp4.MXFP8, n, n)
+                  for _ in range(ROTATE - 1)]
+    qb = [qb0] + [fp4.Quantized(qb0.codes.clone(), qb0.scales.clone(), None, fp4.MXFP4, n, n)
+                  for _ in range(ROTATE - 1)]
+    C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    ms = time_steps(torch, lambda i: fp4.gemm_w4a8(qa[i % ROTATE], qb[i % ROTATE], out=C), 30, 5)
+    tf = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 4), "TFLOP_per_s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "step": "MXFP8 (E4M3) x MXFP4 GEMM, FP32 accumulation, BF16 out (fp4_gemm_w4a8)"}
+
+
+def mxfp8_quantize_8192(torch, fp4, a):
+    x = to_dev(torch, a)
+    q = fp4.quantize(x, fp4.MXFP8)
+    ms = time_steps(torch, lambda i: fp4.quantize(x, fp4.MXFP8, out=q), 50, 5)
+    n = a.size
+    nbytes = n * 4 + n + n // 32
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"us_per_step": round(ms * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline_gemm(a, b, K, budget_s=12.0):
@@ -460,6 +494,8 @@ def main():
             ("nvfp4_quantize_sr_8192", lambda: nvfp4_quantize_sr_8192(torch, fp4, synth)),
             ("hadamard16_8192", lambda: hadamard16_8192(torch, fp4, synth)),
             ("nvfp4_quantize_2d_weight", lambda: nvfp4_quantize_2d_weight(torch, fp4, synth)),
+            ("w4a8_gemm_8192", lambda: w4a8_gemm_8192(torch, fp4, synth, a8192, b8192)),
+            ("mxfp8_quantize_8192", lambda: mxfp8_quantize_8192(torch, fp4, a8192)),
             ("nvfp4_decode_m1", lambda: nvfp4_decode(torch, fp4, synth, 1)),
             ("nvfp4_decode_m8", lambda: nvfp4_decode(torch, fp4, synth, 8)),
             ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),

@@ -2,7 +2,7 @@
 for AMD Instinct MI355X (gfx950).
 
 The C ABI (include/fp4.h) is exposed under the same names (``fp4_quantize``,
-``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_ex``, ``fp4_gemm_grouped``, ``fp4_scale_bytes``,
+``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_ex``, ``fp4_gemm_grouped``, ``fp4_gemm_w4a8``, ``fp4_scale_bytes``,
 ``fp4_workspace_size``, ``fp4_status_string``), taking raw device pointers as
 integers.  The tensor helpers below only allocate outputs with torch and
 marshal ``data_ptr()`` / the current stream into those calls: every step of the
@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp4.so")
 
 # enum fp4_fmt / fp4_dtype / fp4_op, flags
-MXFP4, NVFP4, MXFP4_OCP = 0, 1, 2
+MXFP4, NVFP4, MXFP4_OCP, MXFP8, MXFP8_OCP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 TS_GIVEN = 1
@@ -27,7 +27,8 @@ ACT_NONE, ACT_RELU = 0, 1
 
 FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_sr", "fp4_quantize_ex",
              "fp4_hadamard16", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
-             "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_status_string")
+             "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_gemm_w4a8",
+             "fp4_status_string")
 
 
 class Fp4Error(RuntimeError):
@@ -60,6 +61,7 @@ def lib():
             "fp4_gemm_grouped": (I32, [P, P, I64, P, P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_nvfp4_act": (I32, [P, I32, P, U32, P, P, P, P, I64, I64, I64, I32, P]),
             "fp4_gemm_nvfp4_act_supported": (I32, [I64, I64, I64, I32]),
+            "fp4_gemm_w4a8": (I32, [P, P, P, P, P, I32, P, I64, I64, I64, I32, P]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
         }
         for name, (res, args) in sig.items():
@@ -131,6 +133,10 @@ def fp4_gemm_nvfp4_act_supported(M, N, K, x_dtype):
     return lib().fp4_gemm_nvfp4_act_supported(M, N, K, x_dtype)
 
 
+def fp4_gemm_w4a8(A, sA, B, sB, bias, act, C, M, N, K, out_dtype, stream):
+    return lib().fp4_gemm_w4a8(A, sA, B, sB, bias, act, C, M, N, K, out_dtype, stream)
+
+
 # ---- torch helpers: allocation + pointer/stream marshalling only -------------
 def _torch():
     import torch
@@ -168,8 +174,13 @@ def workspace(op, fmt, M, N, K, E=0, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
+def is_fp8(fmt):
+    """MXFP8 formats hold one E4M3 byte per element (the FP4 ones two codes per byte)."""
+    return fmt in (MXFP8, MXFP8_OCP)
+
+
 class Quantized:
-    """codes (rows x K/2 uint8), scales (tiled uint8), tensor_scale (1 float32 or None)."""
+    """codes (rows x K/2 uint8; MXFP8 rows x K), scales (tiled uint8), tensor_scale (1 float32 or None)."""
 
     def __init__(self, codes, scales, tensor_scale, fmt, rows, K):
         self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
@@ -180,14 +191,15 @@ def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=
     """Quantise a 2-D float32/bfloat16 CUDA tensor along its last dimension.
 
     NVFP4: pass `tensor_scale` (a 1-element float32 tensor) to use a given
-    scale; otherwise one is computed and returned in the result.  sr_seed:
+    scale; otherwise one is computed and returned in the result.  MXFP8 /
+    MXFP8_OCP: E4M3 codes, one byte per element.  sr_seed:
     round the elements stochastically with that seed (fp4_quantize_sr).
     two_d: NVFP4 scales per 16 x 16 patch (fp4_quantize_ex, FP4_Q_2D)."""
     torch = _torch()
     rows, K = x.shape
     dev = x.device
     if out is None:
-        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+        codes = torch.empty((rows, K if is_fp8(fmt) else K // 2), dtype=torch.uint8, device=dev)
         nbytes = fp4_scale_bytes(fmt, rows, K)
         if nbytes < 0:
             raise Fp4Error(int(nbytes), "fp4_scale_bytes")
@@ -281,6 +293,21 @@ def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
                      _ptr(b.tensor_scale), _ptr(bias), act, cptr, sptr, M, N, K, a.fmt, out, _stream(stream))
     _check(rc, "fp4_gemm_ex")
     return C
+
+
+def gemm_w4a8(a, b, bias=None, act=ACT_NONE, out_dtype=None, out=None, stream=None):
+    """C = act(A . B^T + bias) for MXFP8 activations A (M x K) and MXFP4
+    weights B (N x K), FP32 accumulation (see fp4_gemm_w4a8 in include/fp4.h)."""
+    torch = _torch()
+    M, N, K = a.rows, b.rows, a.K
+    if b.K != K or not is_fp8(a.fmt) or b.fmt not in (MXFP4, MXFP4_OCP):
+        raise ValueError("A must be MXFP8 and B MXFP4 with the same K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=a.codes.device)
+    rc = fp4_gemm_w4a8(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(bias), act, _ptr(out),
+                       M, N, K, _dtype_code(out), _stream(stream))
+    _check(rc, "fp4_gemm_w4a8")
+    return out
 
 
 def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_scale=None, out_dtype=None,

@@ -11,7 +11,11 @@
 
 namespace {
 
+// FP4 formats (every GEMM operand of fp4_gemm*), and the quantiser's formats
+// (those plus MXFP8).
 bool fmt_ok(int fmt) { return fmt == FP4_MXFP4 || fmt == FP4_NVFP4 || fmt == FP4_MXFP4_OCP; }
+bool is_mx8(int fmt) { return fmt == FP4_MXFP8 || fmt == FP4_MXFP8_OCP; }
+bool qfmt_ok(int fmt) { return fmt_ok(fmt) || is_mx8(fmt); }
 bool dtype_ok(int dt) { return dt == FP4_F32 || dt == FP4_BF16; }
 int64_t block_of(int fmt) { return fmt == FP4_NVFP4 ? 16 : 32; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -24,14 +28,21 @@ constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 
 int launched(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 
+// The FP4 GEMM kernels address an operand's scale buffer (and the grouped
+// kernel all of A) through 32-bit buffer ranges.
+constexpr int64_t kMaxRange = (int64_t(1) << 32) - 1;
+bool scales_fit(int fmt, int64_t rows, int64_t K) {
+  return ((rows + 31) / 32) * ((K + 255) / 256) * (fmt == FP4_NVFP4 ? 512 : 256) <= kMaxRange;
+}
+
 }  // namespace
 
 extern "C" {
 
 int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K) {
-  if (!fmt_ok(fmt)) return FP4_ERR_FMT;
+  if (!qfmt_ok(fmt)) return FP4_ERR_FMT;
   if (rows < 0 || K < 0 || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
-  // Tiles of 32 rows x 256 K values: 256 bytes (MXFP4) or 512 bytes (NVFP4).
+  // Tiles of 32 rows x 256 K values: 256 bytes (MXFP4, MXFP8) or 512 bytes (NVFP4).
   return ((rows + 31) / 32) * ((K + 255) / 256) * (fmt == FP4_NVFP4 ? 512 : 256);
 }
 
@@ -51,10 +62,11 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
 static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                          int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
                          size_t workspace_bytes, uint64_t seed, void* stream) {
-  if (!fmt_ok(fmt)) return FP4_ERR_FMT;
+  if (!qfmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
   if (flags & ~(FP4_TS_GIVEN | FP4_Q_SR | FP4_Q_2D)) return FP4_ERR_FLAGS;
   if ((flags & FP4_Q_2D) && fmt != FP4_NVFP4) return FP4_ERR_FMT;
+  if ((flags & FP4_Q_SR) && is_mx8(fmt)) return FP4_ERR_FMT;
   const bool sr = (flags & FP4_Q_SR) != 0u, twod = (flags & FP4_Q_2D) != 0u;
   if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
   if (rows * K > (int64_t(1) << 40)) return FP4_ERR_SHAPE;
@@ -62,7 +74,7 @@ static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_
   if (!x || !codes || !block_scales) return FP4_ERR_NULL;
   const bool nv = fmt == FP4_NVFP4;
   if (nv && !tensor_scale) return FP4_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(block_scales, 4)) return FP4_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(codes, is_mx8(fmt) ? 8 : 4) || !aligned(block_scales, 4)) return FP4_ERR_ALIGN;
   if (nv && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
   const bool compute_ts = nv && !(flags & FP4_TS_GIVEN);
   if (compute_ts) {
@@ -117,14 +129,14 @@ int fp4_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t 
 
 int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt, void* out,
                    int out_dtype, int64_t rows, int64_t K, void* stream) {
-  if (!fmt_ok(fmt)) return FP4_ERR_FMT;
+  if (!qfmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
   if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
   if (rows * K > (int64_t(1) << 40)) return FP4_ERR_SHAPE;
   if (rows == 0 || K == 0) return FP4_OK;
   if (!codes || !block_scales || !out) return FP4_ERR_NULL;
   if (fmt == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;
-  if (!aligned(codes, 4) || !aligned(block_scales, 4) || !aligned(out, 16)) return FP4_ERR_ALIGN;
+  if (!aligned(codes, is_mx8(fmt) ? 8 : 4) || !aligned(block_scales, 4) || !aligned(out, 16)) return FP4_ERR_ALIGN;
   return launched(fp4::launch_dequantize(codes, block_scales, tensor_scale, fmt, out, out_dtype, rows, K,
                                          as_stream(stream)));
 }
@@ -135,7 +147,7 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
   if (!fmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 32 != 0) return FP4_ERR_SHAPE;
-  if (K > kMaxGemmK) return FP4_ERR_SHAPE;
+  if (K > kMaxGemmK || !scales_fit(fmt, M, K) || !scales_fit(fmt, N, K)) return FP4_ERR_SHAPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (!C) return FP4_ERR_NULL;
   if (K > 0 && (!A || !sA || !B || !sB)) return FP4_ERR_NULL;
@@ -158,7 +170,7 @@ int fp4_gemm_ex(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uin
   if (out < FP4_OUT_F32 || out > FP4_OUT_MXFP4_OCP) return FP4_ERR_DTYPE;
   if (act != FP4_ACT_NONE && act != FP4_ACT_RELU) return FP4_ERR_FLAGS;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 32 != 0) return FP4_ERR_SHAPE;
-  if (K > kMaxGemmK) return FP4_ERR_SHAPE;
+  if (K > kMaxGemmK || !scales_fit(fmt, M, K) || !scales_fit(fmt, N, K)) return FP4_ERR_SHAPE;
   const bool fp4_out = out >= FP4_OUT_MXFP4;
   if (fp4_out && N % 32 != 0) return FP4_ERR_SHAPE;
   if (M == 0 || N == 0) return FP4_OK;
@@ -184,6 +196,7 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
   if (E < 0 || A_rows < 0 || total_rows < 0 || N < 0 || K < 0 || A_rows > kMaxDim || total_rows > kMaxDim ||
       N > kMaxDim || K > kMaxGemmK || K % 32 != 0)
     return FP4_ERR_SHAPE;
+  if (!scales_fit(fmt, A_rows, K) || !scales_fit(fmt, N, K) || A_rows * (K / 2) > kMaxRange) return FP4_ERR_SHAPE;
   if (total_rows == 0 || N == 0 || E == 0) return FP4_OK;
   if (!C || !row_idx || !group_off) return FP4_ERR_NULL;
   if (K > 0 && (!A || !sA || !B || !sB)) return FP4_ERR_NULL;
@@ -221,6 +234,22 @@ int fp4_gemm_nvfp4_act(const void* X, int x_dtype, float* x_tensor_scale, unsign
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   return launched(fp4::launch_gemv_nv_fused(X, x_dtype, x_tensor_scale, flags, W, sW, tsW, C, M, N, K, out_dtype,
                                             as_stream(stream)));
+}
+
+int fp4_gemm_w4a8(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* bias,
+                  int act, void* C, int64_t M, int64_t N, int64_t K, int out_dtype, void* stream) {
+  if (!dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
+  if (act != FP4_ACT_NONE && act != FP4_ACT_RELU) return FP4_ERR_FLAGS;
+  // K <= 2^23 keeps a 256-row tile of FP8 codes inside one 32-bit buffer range.
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > (kMaxGemmK >> 1) || K % 32 != 0)
+    return FP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (!C) return FP4_ERR_NULL;
+  if (K > 0 && (!A || !sA || !B || !sB)) return FP4_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, 4) || !aligned(sB, 4) || !aligned(bias, 16))
+    return FP4_ERR_ALIGN;
+  if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
+  return launched(fp4::launch_gemm_w4a8(A, sA, B, sB, bias, act, C, M, N, K, out_dtype, as_stream(stream)));
 }
 
 const char* fp4_status_string(int status) {

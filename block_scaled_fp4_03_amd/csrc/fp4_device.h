@@ -23,6 +23,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFmtMX = 0, kFmtNV = 1, kFmtMXOcp = 2;
+// MXFP8: E4M3 elements (one byte each) under 32-block E8M0 scales.
+constexpr int kFmtMX8 = 3, kFmtMX8Ocp = 4;
 
 // Input / output element types (the C ABI's fp4_dtype values).
 constexpr int kDtF32 = 0, kDtBF16 = 1;
@@ -51,6 +53,34 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   int b = be - 2;
   if (FMT == kFmtMX) b += ((u & 0x7FFFFFu) > 0x400000u) ? 1 : 0;
   return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// E8M0 byte of an MXFP8 block: the MXFP4 rules with E4M3's largest value
+// 448 = 1.75 * 2^8 in place of 6.  Default: the smallest e with
+// amax <= 448 * 2^e, i.e. e = E - 8 if m <= 1.75, else E - 7 (amax = m * 2^E);
+// in FP32 bits byte = max(0, exp_field - 8 + (mantissa > 0x600000)).  OCP:
+// e = floor(log2 amax) - 8, byte = max(0, exp_field - 8).
+template <int FMT>
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  uint32_t u = f2u(amax);
+  int b = (int)(u >> 23) - 8;
+  if (FMT == kFmtMX8) b += ((u & 0x7FFFFFu) > 0x600000u) ? 1 : 0;
+  return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// E4M3 codes of four values (bytes 0..3), each first limited to [-448, 448]
+// (saturation; the conversion itself would give NaN above 448.5), then
+// converted by the hardware, which rounds to nearest even and keeps the sign
+// (-0 -> 0x80).
+__device__ __forceinline__ uint32_t e4m3x4_sat(float a, float b, float c, float d) {
+  const float lim = 448.0f;
+  a = fminf(fmaxf(a, -lim), lim);
+  b = fminf(fmaxf(b, -lim), lim);
+  c = fminf(fmaxf(c, -lim), lim);
+  d = fminf(fmaxf(d, -lim), lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 // E4M3 byte nearest to r >= 0 (ties to even), saturating at 448 (0x7E).

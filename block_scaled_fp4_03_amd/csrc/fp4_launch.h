@@ -53,6 +53,12 @@ hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_ro
 
 // NVFP4 decode GEMV / skinny GEMM for M <= 32 (gemv_nv.hip).
 bool gemv_nv_applies(int64_t M, int64_t N, int64_t K);
+// MXFP8 (A) x MXFP4 (B) tiled GEMM with the bias / ReLU epilogue; out 0 FP32,
+// 1 BF16.
+hipError_t launch_gemm_w4a8(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
+                            const float* bias, int act, void* C, int64_t M, int64_t N, int64_t K, int out,
+                            hipStream_t stream);
+
 hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                           int out_dtype, hipStream_t stream);

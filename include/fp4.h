@@ -13,7 +13,10 @@
  *     C = (A_fp4 * B_fp4) * (scaleA * scaleB) ("Rubin FP4 GEMM deep dive",
  *     yfxerp.com, §1.1, §3.1, §4.2);
  *   - two FP4 values per byte with an explicitly fixed order, scales stored in
- *     the order the kernel tiles read them (same page, §4.2, §5.2).
+ *     the order the kernel tiles read them (same page, §4.2, §5.2);
+ *   - weights and activations may take different precisions, FP8 activations
+ *     beside FP4 weights (same page, §3.4), here MXFP8: E4M3 elements under
+ *     the MXFP4 block scales (§3.1 names MXFP8 among the MX formats).
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent) unless
@@ -32,18 +35,24 @@
  *               with magnitude 0..7 -> 0, 0.5, 1, 1.5, 2, 3, 4, 6;
  *       scales: fp4_scale_bytes(fmt, rows, K) bytes in the tiled layout below;
  *       tensor scale (NVFP4 only): one FP32 in device memory.
+ *     MXFP8 codes are rows * K bytes instead, one E4M3 byte per element
+ *     (sign<<7 | exponent<<3 | mantissa, bias 7, largest value 448; the NaN
+ *     patterns 0x7F / 0xFF are never written and not supported as input).
  *   - Element value: MXFP4  E2M1(code) * 2^(scale_byte - 127);
+ *                    MXFP8  E4M3(code) * 2^(scale_byte - 127);
  *                    NVFP4  E2M1(code) * E4M3(scale_byte) * tensor_scale.
  *
  * Tiled scale layout (identical for A and B operands; both are "rows x K").
  *   Scales are grouped in tiles of 32 rows x 256 K values, stored row-tile
  *   major: tile (rt, kt) starts at byte T * (rt * ceil(K/256) + kt), with tile
- *   size T = 256 (MXFP4: 8 blocks of 32) or 512 (NVFP4: 16 blocks of 16).
+ *   size T = 256 (MXFP4 and MXFP8: 8 blocks of 32) or 512 (NVFP4: 16 blocks
+ *   of 16).
  *   Inside a tile, row i (0..31) and 32-value K chunk c (0..7) belong to lane
  *   L = 32 * (c % 2) + i and sub-step s = c / 2 -- the lane order of the 32x32
  *   matrix-core operand, where lane 32*j + i carries row i's chunk j of each
  *   64-value K sub-step:
- *     MXFP4: lane L owns bytes 4L..4L+3; byte 4L + s is the chunk's E8M0 scale;
+ *     MXFP4, MXFP8: lane L owns bytes 4L..4L+3; byte 4L + s is the chunk's
+ *            E8M0 scale;
  *     NVFP4: lane L owns bytes 8L..8L+7; bytes 8L + 2s and 8L + 2s + 1 are the
  *            E4M3 scales of the chunk's first and second 16-value block.
  *   One dword (MXFP4) or two (NVFP4) per lane thus carry a wavefront's scales
@@ -67,7 +76,9 @@ extern "C" {
 enum fp4_fmt {
     FP4_MXFP4 = 0,     /* 32-blocks, E8M0; exponent = smallest e with amax <= 6*2^e */
     FP4_NVFP4 = 1,     /* 16-blocks, E4M3 (bias 7, max 448) + FP32 tensor scale      */
-    FP4_MXFP4_OCP = 2  /* 32-blocks, E8M0; exponent = floor(log2 amax) - 2, saturate */
+    FP4_MXFP4_OCP = 2, /* 32-blocks, E8M0; exponent = floor(log2 amax) - 2, saturate */
+    FP4_MXFP8 = 3,     /* 32-blocks, E8M0, E4M3 elements; smallest e with amax <= 448*2^e */
+    FP4_MXFP8_OCP = 4  /* 32-blocks, E8M0, E4M3 elements; floor(log2 amax) - 8, saturate */
 };
 
 /* Element type of unquantised inputs and of outputs. */
@@ -119,7 +130,9 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
 size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E);
 
 /* Quantise a rows x K matrix x (K contiguous) of `in_dtype` (FP32 or BF16).
- *   Per block: MXFP4 picks an E8M0 exponent from the block's largest magnitude;
+ *   Per block: MXFP4 picks an E8M0 exponent from the block's largest magnitude
+ *   (MXFP8: the same rules with 448 in place of 6, elements y = x * 2^-e
+ *   rounded to the nearest E4M3 value, ties to even, saturating at 448);
  *   NVFP4 takes r = (amax_block / 6) / tensor_scale, rounds it to E4M3 (nearest
  *   even, saturating at 448), and divides by d = E4M3(r) * tensor_scale (FP32).
  *   Each element is then rounded to the nearest E2M1 value, ties to even,
@@ -129,8 +142,8 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
  *   s_t >= FLT_MIN, and written to *tensor_scale.  With FP4_TS_GIVEN the caller's
  *   value is used (it must be a positive, finite, normal FP32).
  *   (Sources: glossary "How FP4 works"; NVFP4 video transcript.)
- * Requirements: K % bs == 0 (32 for MXFP4, 16 for NVFP4); x 16-byte aligned;
- *   codes and block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
+ * Requirements: K % bs == 0 (32 for MXFP4 and MXFP8, 16 for NVFP4); x 16-byte
+ *   aligned; codes 4-byte (MXFP8: 8-byte) and block_scales 4-byte aligned.  tensor_scale must be non-NULL for NVFP4 and
  *   is ignored for MXFP4.  NVFP4 without FP4_TS_GIVEN needs a workspace of
  *   fp4_workspace_size(FP4_OP_QUANTIZE, ...) bytes; otherwise workspace may be NULL.
  *   (Inputs of at most 256 KB take a single launch in which every workgroup
@@ -155,7 +168,8 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
  * easy as 1, 2, 3", SC 2011) with key (seed, 0); element i of the matrix
  * (row-major, i = r * K + k) takes word (i mod 8) / 2 of the block with
  * counter (i / 8, 0, 0, 0), its low 32 bits for even i.  The result is a
- * function of (x, seed) alone.  Arguments and errors as fp4_quantize. */
+ * function of (x, seed) alone.  FP4 formats only (MXFP8: FP4_ERR_FMT).
+ * Arguments and errors as fp4_quantize. */
 int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                     int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
                     size_t workspace_bytes, void* stream);
@@ -199,7 +213,8 @@ int fp4_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t 
 /* Dequantise codes + scales (+ NVFP4 tensor scale) to a rows x K matrix of
  * `out_dtype`.  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,
  * times tensor_scale with one FP32 rounding; BF16 output is the round-to-
- * nearest-even of that FP32 value.  Same alignment rules as fp4_quantize. */
+ * nearest-even of that FP32 value.  MXFP8 values are exact.  Same alignment
+ * rules as fp4_quantize. */
 int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt,
                    void* out, int out_dtype, int64_t rows, int64_t K, void* stream);
 
@@ -217,8 +232,11 @@ int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const floa
  *   while the activation fits the workgroup's staging memory (for example
  *   M <= 8 with K <= 8960, or any M <= 32 with K <= 8192); larger shapes take
  *   the tiled kernel.
+ * Formats: the FP4 ones (MXFP8 operands: fp4_gemm_w4a8).
  * Requirements: K % 32 == 0 (both formats); codes 16-byte aligned; scales
- *   4-byte aligned; C aligned to its element size.  M, N >= 0 arbitrary.
+ *   4-byte aligned; C aligned to its element size.  M, N >= 0 arbitrary, as
+ *   long as each operand's scale buffer stays below 4 GiB (at K = 8192:
+ *   2^24 rows for MXFP4, 2^23 for NVFP4).
  *   workspace: fp4_workspace_size(FP4_OP_GEMM, fmt, M, N, K, 0) bytes,
  *   zero-filled before first use (0 bytes -> NULL is fine).
  * M == 0 or N == 0 is a no-op; K == 0 writes zeros. */
@@ -238,7 +256,8 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
  *   Group sizes stay on the device; the kernel builds its own tile list.
  *   Every row_idx entry must lie in [0, A_rows).
  * Formats: FP4_MXFP4 and FP4_MXFP4_OCP; FP4_NVFP4 returns FP4_ERR_FMT.
- * Requirements as fp4_gemm; workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
+ * Requirements as fp4_gemm, and A's codes (A_rows * K/2 bytes) below 4 GiB;
+ *   workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
  *   fmt, total_rows, N, K, E) bytes (0 today). */
 int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                      const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
@@ -291,6 +310,25 @@ int fp4_gemm_nvfp4_act_supported(int64_t M, int64_t N, int64_t K, int x_dtype);
 int fp4_gemm_ex(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* tsA,
                 const float* tsB, const float* bias, int act, void* C, uint8_t* C_scales, int64_t M, int64_t N,
                 int64_t K, int fmt, int out, void* stream);
+
+/* Mixed-format GEMM, W4A8 ("Rubin FP4 GEMM deep dive" §3.4: activations
+ * kept in FP8 while the weights go to FP4):
+ *   C[m,n] = sum_k A[m,k] * B[n,k], accumulated in FP32, then
+ *   v = v + bias[n] (bias != NULL) and v = v > 0 ? v : +0 (act ==
+ *   FP4_ACT_RELU), each step one FP32 rounding, stored as FP32 or BF16
+ *   (out_dtype, round to nearest even).
+ *   A: M x K MXFP8 (codes M * K bytes, scales fp4_scale_bytes(FP4_MXFP8, M, K)
+ *   bytes), as fp4_quantize(FP4_MXFP8 or FP4_MXFP8_OCP) writes them.
+ *   B: N x K MXFP4 (either exponent rule), as for fp4_gemm.
+ * The gfx950 block-scaled matrix core multiplies E4M3 by E2M1 directly, both
+ * E8M0 scales applied inside the instruction (at the FP8 rate, half the FP4
+ * rate).
+ * Requirements: K % 32 == 0, K <= 2^23; codes 16-byte aligned; scales 4-byte
+ *   aligned; bias 16-byte aligned or NULL; C aligned to its element size.
+ *   M, N >= 0 arbitrary.  No workspace.
+ * M == 0 or N == 0 is a no-op; K == 0 gives v = 0 (+ bias, activation). */
+int fp4_gemm_w4a8(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* bias,
+                  int act, void* C, int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
 
 /* Static string naming a status code. */
 const char* fp4_status_string(int status);

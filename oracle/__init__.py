@@ -10,7 +10,8 @@ Definitions follow the pages cited in ``fp4_oracle.c``: the E2M1 grid and the
 block-max-to-6 rule (Ultralytics glossary "FP4", "How FP4 works"), MXFP4 and
 NVFP4 block formats (NVFP4 video transcript, prism.simon-ai.net), E8M0 scales
 and the scaled FP32-accumulated GEMM ("Rubin FP4 GEMM deep dive",
-yfxerp.com, §3.1, §4.2).
+yfxerp.com, §3.1, §4.2), and MXFP8 operands beside MXFP4 ones (same page, §3.4:
+activations kept in FP8 while weights go to FP4).
 
 Parity pins: every function here is pinned by a non-GPU test in
 ``tests/test_oracle_pins.py`` / ``tests/test_codecs.py`` (printed worked example,
@@ -27,7 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "fp4_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-FMT_MXFP4, FMT_NVFP4, FMT_MXFP4_OCP = 0, 1, 2
+FMT_MXFP4, FMT_NVFP4, FMT_MXFP4_OCP, FMT_MXFP8, FMT_MXFP8_OCP = 0, 1, 2, 3, 4
 DT_F32, DT_BF16 = 0, 1
 
 _lib = None
@@ -57,6 +58,8 @@ def lib():
             "oracle_e8m0_value": (D, [I32]),
             "oracle_mx_exponent": (I32, [F]),
             "oracle_mx_exponent_ocp": (I32, [F]),
+            "oracle_mx8_exponent": (I32, [F]),
+            "oracle_mx8_exponent_ocp": (I32, [F]),
             "oracle_e4m3_value": (D, [I32]),
             "oracle_e4m3_encode": (I32, [F]),
             "oracle_f32_to_bf16": (ctypes.c_uint16, [F]),
@@ -74,6 +77,8 @@ def lib():
             "oracle_e2m1_sr_mag": (I32, [F, ctypes.c_uint32]),
             "oracle_dequantize": (None, [P, P, P, I32, P, I32, I64, I64]),
             "oracle_gemm": (None, [P, P, P, P, D, D, I64, I64, I64, I32, P, P]),
+            "oracle_gemm_mixed": (None, [P, P, I32, P, P, I32, D, D, I64, I64, I64, P, P]),
+            "oracle_gemm_mixed_sampled": (None, [P, P, I32, P, P, I32, D, D, I64, I64, I64, P, P, I64, P, P]),
             "oracle_epilogue": (None, [P, P, I32, I64, I64, P]),
             "oracle_gemm_sampled": (None, [P, P, P, P, D, D, I64, I64, I64, I32, P, P, I64, P, P]),
             "oracle_gemm_grouped_sampled": (None, [P, P, I64, P, P, I32, P, P, D, D, I64, I64, I32,
@@ -98,6 +103,15 @@ def _p(a):
 
 def block_size(fmt):
     return 16 if fmt == FMT_NVFP4 else 32
+
+
+def is_fp8(fmt):
+    """MXFP8 formats store one E4M3 byte per element (FP4: two per byte)."""
+    return fmt in (FMT_MXFP8, FMT_MXFP8_OCP)
+
+
+def code_bytes(fmt, rows, K):
+    return rows * K if is_fp8(fmt) else rows * K // 2
 
 
 # ---- scalar codecs -------------------------------------------------------
@@ -134,6 +148,13 @@ def mx_exponent(amax, ocp=False):
     return out
 
 
+def mx8_exponent(amax, ocp=False):
+    """MXFP8 block exponent of each amax (scalar loop over the C function)."""
+    a = np.ascontiguousarray(amax, dtype=np.float32).ravel()
+    fn = lib().oracle_mx8_exponent_ocp if ocp else lib().oracle_mx8_exponent
+    return np.array([fn(float(v)) for v in a], np.int32).reshape(np.shape(amax))
+
+
 def f32_to_bf16_bits(f):
     f = np.ascontiguousarray(f, dtype=np.float32)
     out = np.empty(f.shape, np.uint16)
@@ -157,8 +178,9 @@ def scale_offset(fmt, rows, K, r, b):
 def quantize(x, fmt, tensor_scale=None, sr_seed=None, two_d=False):
     """x: (rows, K) float32, or uint16 holding BF16 bit patterns.
 
-    Returns (codes[rows, K//2] u8, scales[tiled] u8, scales_canon[rows, K//bs] u8,
-    tensor_scale float) -- tensor_scale is 1.0 for MXFP4.  sr_seed: round the
+    Returns (codes[rows, K//2] u8 (MXFP8: [rows, K]), scales[tiled] u8,
+    scales_canon[rows, K//bs] u8, tensor_scale float) -- tensor_scale is 1.0 for
+    the MX formats.  sr_seed: round the
     elements stochastically with that seed (scales unchanged).  two_d: NVFP4
     block scales shared by 16 x 16 patches."""
     x = np.ascontiguousarray(x)
@@ -167,7 +189,7 @@ def quantize(x, fmt, tensor_scale=None, sr_seed=None, two_d=False):
         x = x.astype(np.float32, copy=False)
     rows, K = x.shape
     bs = block_size(fmt)
-    codes = np.zeros((rows, K // 2), np.uint8)
+    codes = np.zeros((rows, K if is_fp8(fmt) else K // 2), np.uint8)
     scales = np.zeros(scale_bytes(fmt, rows, K), np.uint8)
     canon = np.zeros((rows, K // bs), np.uint8)
     ts = np.array([1.0 if tensor_scale is None else tensor_scale], np.float32)
@@ -256,6 +278,27 @@ def epilogue(C, bias=None, act=ACT_NONE):
     out = np.empty((M, N), np.float32)
     lib().oracle_epilogue(_p(C), _p(b), int(act), M, N, _p(out))
     return out
+
+
+def gemm_mixed(A, sA, fmtA, B, sB, fmtB, M, N, K, tsA=1.0, tsB=1.0):
+    """As gemm, with A in format fmtA and B in fmtB (e.g. MXFP8 x MXFP4)."""
+    C = np.empty((M, N), np.float64)
+    T = np.empty((M, N), np.float64)
+    lib().oracle_gemm_mixed(_p(np.ascontiguousarray(A)), _p(np.ascontiguousarray(sA)), fmtA,
+                            _p(np.ascontiguousarray(B)), _p(np.ascontiguousarray(sB)), fmtB,
+                            float(tsA), float(tsB), M, N, K, _p(C), _p(T))
+    return C, T
+
+
+def gemm_mixed_sampled(A, sA, fmtA, B, sB, fmtB, M, N, K, rows, cols, tsA=1.0, tsB=1.0):
+    rows = np.ascontiguousarray(rows, np.int64)
+    cols = np.ascontiguousarray(cols, np.int64)
+    C = np.empty(rows.size, np.float64)
+    T = np.empty(rows.size, np.float64)
+    lib().oracle_gemm_mixed_sampled(_p(np.ascontiguousarray(A)), _p(np.ascontiguousarray(sA)), fmtA,
+                                    _p(np.ascontiguousarray(B)), _p(np.ascontiguousarray(sB)), fmtB,
+                                    float(tsA), float(tsB), M, N, K, _p(rows), _p(cols), rows.size, _p(C), _p(T))
+    return C, T
 
 
 def gemm_sampled(A, sA, B, sB, M, N, K, fmt, rows, cols, tsA=1.0, tsB=1.0):

@@ -17,6 +17,8 @@
  *        §3.1 E2M1 with one mantissa bit, block scaling, E8M0 power-of-two
  *        scales, GEMM result times the product of the two scales;
  *        §4.2 epilogue C = (A_fp4 * B_fp4) * (scaleA * scaleB);
+ *        §3.4 weights and activations may take different precisions
+ *        (activations kept in FP8 while weights go to FP4);
  *        §5.2 two FP4 values per byte, order must be fixed explicitly.
  *   [P2] NVFP4 video transcript (prism.simon-ai.net/article/7890):
  *        MXFP4 = 32-value blocks with a power-of-two scale (a scale of 70
@@ -33,7 +35,10 @@
  * smallest e with amax <= 6 * 2^e ("ceil"), with the OCP-style
  * floor(log2 amax) - 2 rule as a second mode; E4M3 = bias 7, max 448, no
  * infinities, rounding to nearest-even with saturation; NVFP4 tensor scale
- * s_t = amax_t / (6 * 448); low nibble holds the even-K element.
+ * s_t = amax_t / (6 * 448); low nibble holds the even-K element.  MXFP8
+ * (the FP8 operand of a mixed product, [P1] §3.1 names MXFP8 beside MXFP4):
+ * E4M3 elements, one byte each, under 32-block E8M0 scales chosen by the
+ * MXFP4 rules with 448 in place of 6.
  */
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +48,9 @@
 #define OR_FMT_MXFP4 0
 #define OR_FMT_NVFP4 1
 #define OR_FMT_MXFP4_OCP 2
+#define OR_FMT_MXFP8 3
+#define OR_FMT_MXFP8_OCP 4
+#define IS_MX8(fmt) ((fmt) == OR_FMT_MXFP8 || (fmt) == OR_FMT_MXFP8_OCP)
 
 #define OR_DT_F32 0
 #define OR_DT_BF16 1
@@ -159,6 +167,35 @@ int oracle_e4m3_encode(float r)
         }
     }
     return best;
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 scale ([P1] §3.1: MX formats share one power-of-two E8M0 scale per
+ * block; §3.4: FP8 activations beside FP4 weights).  The MXFP4 rules with
+ * E4M3's largest value 448 (= 1.75 * 2^8) in place of 6:
+ *   default: the smallest e in [-127, 127] with amax <= 448 * 2^e, found
+ *            by counting upward, exactly in FP64 (no element clips);
+ *   OCP:     e = floor(log2 amax) - 8, 8 being E4M3's largest exponent,
+ *            clamped; scaled elements above 448 then saturate to 448.   */
+/* ------------------------------------------------------------------ */
+int oracle_mx8_exponent(float amax)
+{
+    int e = -127;
+    while (e < 127 && (double)amax > 448.0 * ldexp(1.0, e))
+        ++e;
+    return e;
+}
+
+int oracle_mx8_exponent_ocp(float amax)
+{
+    if (amax == 0.0f)
+        return -127;
+    int ex;
+    (void)frexp((double)amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+    int e = (ex - 1) - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
 }
 
 /* ------------------------------------------------------------------ */
@@ -360,6 +397,16 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
                          : oracle_e2m1_encode_mag(y);
             codes_out[k] = (uint8_t)(sign | mag);
         }
+    } else if (IS_MX8(rule)) {
+        /* MXFP8: y = |x| * 2^-e (exact), E4M3 byte nearest to y with ties
+         * to even, saturating at 448; bit 7 = the input's sign bit. */
+        int e = (rule == OR_FMT_MXFP8_OCP) ? oracle_mx8_exponent_ocp(amax) : oracle_mx8_exponent(amax);
+        sbyte = e + 127;
+        for (int k = 0; k < bs; ++k) {
+            int sign = signbit(v[k]) ? 0x80 : 0;
+            float y = ldexpf(fabsf(v[k]), -e);
+            codes_out[k] = (uint8_t)(sign | oracle_e4m3_encode(y));
+        }
     } else {
         int e = (rule == OR_FMT_MXFP4_OCP) ? oracle_mx_exponent_ocp(amax) : oracle_mx_exponent(amax);
         sbyte = e + 127;
@@ -376,7 +423,8 @@ static int quantize_block(const float* v, int bs, int rule, float s_t, uint8_t* 
 
 /* Quantise a rows x K matrix (K contiguous).
  *   codes:  rows x K/2 bytes, element 2i in bits 0-3 of byte i, 2i+1 in
- *           bits 4-7 ([P1] §5.2 leaves the order open; this is the reading).
+ *           bits 4-7 ([P1] §5.2 leaves the order open; this is the reading);
+ *           MXFP8: rows x K bytes, one E4M3 byte per element.
  *   scales: the tiled layout above (oracle_scale_bytes bytes), or, when
  *           scales_canon is non-NULL, additionally rows x K/bs canonical.
  *   tensor_scale: NVFP4 only.  If ts_given, *tensor_scale is read;
@@ -398,6 +446,8 @@ static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t
         return -1;
     if (twod && fmt != OR_FMT_NVFP4)
         return -1;
+    if (sr && IS_MX8(fmt))
+        return -1;   /* stochastic rounding is defined for the E2M1 grid only */
     float s_t = 1.0f;
     if (fmt == OR_FMT_NVFP4) {
         if (ts_given) {
@@ -429,8 +479,13 @@ static int quantize_matrix(const void* x, int dt, int fmt, int64_t rows, int64_t
             scales[oracle_scale_offset(fmt, rows, K, r, b)] = (uint8_t)sb;
             if (scales_canon)
                 scales_canon[r * KB + b] = (uint8_t)sb;
-            for (int k = 0; k < bs; k += 2)
-                codes[(r * K + b * bs + k) / 2] = (uint8_t)(c[k] | (c[k + 1] << 4));
+            if (IS_MX8(fmt)) {
+                for (int k = 0; k < bs; ++k)
+                    codes[r * K + b * bs + k] = c[k];   /* one byte per element */
+            } else {
+                for (int k = 0; k < bs; k += 2)
+                    codes[(r * K + b * bs + k) / 2] = (uint8_t)(c[k] | (c[k + 1] << 4));
+            }
         }
     }
     return 0;
@@ -493,19 +548,23 @@ void oracle_rht16(const void* x, int dt, int64_t rows, int64_t K, uint64_t seed,
 }
 
 /* Exact value of element (r, k) of a quantised matrix, without the tensor
- * scale: E2M1(code) * block scale ([P4]: grid * sign * scale). */
+ * scale: E2M1(code) * block scale ([P4]: grid * sign * scale); MXFP8:
+ * E4M3(byte) * 2^(scale byte - 127). */
 static double elem_value(const uint8_t* codes, const uint8_t* scales, int fmt, int64_t rows, int64_t K,
                          int64_t r, int64_t k)
 {
     int bs = (int)block_size(fmt);
+    int sb = scales[oracle_scale_offset(fmt, rows, K, r, k / bs)];
+    if (IS_MX8(fmt))
+        return oracle_e4m3_value(codes[r * K + k]) * oracle_e8m0_value(sb);
     uint8_t byte = codes[(r * K + k) / 2];
     int code = (k & 1) ? (byte >> 4) : (byte & 15);
-    int sb = scales[oracle_scale_offset(fmt, rows, K, r, k / bs)];
     double s = (fmt == OR_FMT_NVFP4) ? oracle_e4m3_value(sb) : oracle_e8m0_value(sb);
     return oracle_e2m1_value(code) * s;
 }
 
-/* Dequantise to FP32 or BF16.  MXFP4: E2M1 * 2^(byte-127), exact.  NVFP4:
+/* Dequantise to FP32 or BF16.  MXFP4: E2M1 * 2^(byte-127), exact (MXFP8
+ * likewise, for the scale bytes the quantiser produces).  NVFP4:
  * (E2M1 * E4M3) * s_t -- the first product is exact, the second is one
  * FP32 rounding.  BF16 output is the round-to-nearest-even of that FP32. */
 void oracle_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int fmt,
@@ -534,8 +593,10 @@ void oracle_dequantize(const uint8_t* codes, const uint8_t* scales, const float*
  * B is N x K (one row per output column).  T bounds accumulation error:
  * a result is accepted when |C - Cref| <= 1e-5 * T.                     */
 /* ------------------------------------------------------------------ */
-void oracle_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
-                 double tsB, int64_t M, int64_t N, int64_t K, int fmt, double* C, double* T)
+/* Mixed operands ([P1] §3.4: A and B in different formats, e.g. FP8
+ * activations times FP4 weights): A in format fmtA, B in fmtB. */
+void oracle_gemm_mixed(const uint8_t* A, const uint8_t* sA, int fmtA, const uint8_t* B, const uint8_t* sB,
+                       int fmtB, double tsA, double tsB, int64_t M, int64_t N, int64_t K, double* C, double* T)
 {
     double ts = tsA * tsB;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -543,13 +604,19 @@ void oracle_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const ui
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                double p = elem_value(A, sA, fmt, M, K, m, k) * elem_value(B, sB, fmt, N, K, n, k);
+                double p = elem_value(A, sA, fmtA, M, K, m, k) * elem_value(B, sB, fmtB, N, K, n, k);
                 acc += p;
                 mag += fabs(p);
             }
             C[m * N + n] = acc * ts;
             if (T) T[m * N + n] = mag * fabs(ts);
         }
+}
+
+void oracle_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
+                 double tsB, int64_t M, int64_t N, int64_t K, int fmt, double* C, double* T)
+{
+    oracle_gemm_mixed(A, sA, fmt, B, sB, fmt, tsA, tsB, M, N, K, C, T);
 }
 
 /* ------------------------------------------------------------------ */
@@ -577,22 +644,30 @@ void oracle_epilogue(const double* C, const float* bias, int act, int64_t M, int
 
 /* Only the listed output elements (rows[i], cols[i]); for sampled checks at
  * sizes where the full product would take too long on the CPU. */
-void oracle_gemm_sampled(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
-                         double tsB, int64_t M, int64_t N, int64_t K, int fmt, const int64_t* rows,
-                         const int64_t* cols, int64_t count, double* C, double* T)
+void oracle_gemm_mixed_sampled(const uint8_t* A, const uint8_t* sA, int fmtA, const uint8_t* B,
+                               const uint8_t* sB, int fmtB, double tsA, double tsB, int64_t M, int64_t N,
+                               int64_t K, const int64_t* rows, const int64_t* cols, int64_t count, double* C,
+                               double* T)
 {
     double ts = tsA * tsB;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < count; ++i) {
         double acc = 0.0, mag = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double p = elem_value(A, sA, fmt, M, K, rows[i], k) * elem_value(B, sB, fmt, N, K, cols[i], k);
+            double p = elem_value(A, sA, fmtA, M, K, rows[i], k) * elem_value(B, sB, fmtB, N, K, cols[i], k);
             acc += p;
             mag += fabs(p);
         }
         C[i] = acc * ts;
         if (T) T[i] = mag * fabs(ts);
     }
+}
+
+void oracle_gemm_sampled(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, double tsA,
+                         double tsB, int64_t M, int64_t N, int64_t K, int fmt, const int64_t* rows,
+                         const int64_t* cols, int64_t count, double* C, double* T)
+{
+    oracle_gemm_mixed_sampled(A, sA, fmt, B, sB, fmt, tsA, tsB, M, N, K, rows, cols, count, C, T);
 }
 
 /* Grouped product for mixture-of-experts layers ([P4], "Inference and

@@ -219,3 +219,47 @@ def test_quantize_ex_and_hadamard_argument_errors(L):
     assert h(None, 0, FAKE, 0, 4, 64, 0, None) == -1
     assert h(FAKE + 8, 0, FAKE, 0, 4, 64, 0, None) == -3
     assert h(FAKE, 0, FAKE, 0, 0, 64, 0, None) == 0
+
+
+def test_w4a8_and_mxfp8_argument_errors(L):
+    """fp4_gemm_w4a8 and the MXFP8 formats reject bad arguments before any HIP
+    call (fake pointers)."""
+    g = fp4.fp4_gemm_w4a8
+
+    def call(**kw):
+        a = dict(A=FAKE, sA=FAKE, B=FAKE, sB=FAKE, bias=None, act=0, C=FAKE, M=64, N=64, K=256, out=1)
+        a.update(kw)
+        return g(a["A"], a["sA"], a["B"], a["sB"], a["bias"], a["act"], a["C"], a["M"], a["N"], a["K"], a["out"],
+                 None)
+
+    assert call(out=2) == -5
+    assert call(act=2) == -8
+    assert call(K=48) == -2
+    assert call(K=1 << 24) == -2        # an FP8 tile of 256 rows must stay inside 32-bit ranges
+    assert call(M=-1) == -2
+    assert call(M=0) == 0 and call(N=0) == 0
+    assert call(C=None) == -1
+    assert call(A=None) == -1
+    assert call(A=FAKE + 8) == -3
+    assert call(bias=FAKE + 4) == -3
+    assert call(out=0, C=FAKE + 2) == -3
+    # MXFP8 quantise: no stochastic rounding, codes 8-byte aligned; FP4 GEMMs refuse it
+    assert fp4.fp4_quantize_sr(FAKE, 3, FAKE, FAKE, None, 4, 64, 0, 0, 1, None, 0, None) == -4
+    assert fp4.fp4_quantize(FAKE, 4, FAKE + 4, FAKE, None, 4, 64, 0, 0, None, 0, None) == -3
+    assert fp4.fp4_quantize(FAKE, 5, FAKE, FAKE, None, 4, 64, 0, 0, None, 0, None) == -4
+    assert fp4.fp4_quantize(FAKE, 3, FAKE, FAKE, None, 4, 48, 0, 0, None, 0, None) == -2
+    assert fp4.fp4_dequantize(FAKE + 4, FAKE, None, 3, FAKE, 0, 4, 64, None) == -3   # MXFP8 codes 8-byte aligned
+    assert fp4.fp4_scale_bytes(3, 33, 288) == 2 * 2 * 256
+    assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 64, 64, 256, 3, 1, None, 0, None) == -4
+
+
+def test_gemm_scale_ranges_are_checked(L):
+    """Shapes whose scale buffers would not fit the kernels' 32-bit ranges are
+    refused on the host."""
+    big = 1 << 25      # rows: (2^25 / 32) tiles * 32 K-tiles * 256 B = 2^33 bytes of scales at K = 8192
+    assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, 64, 8192, 0, 1, None, 0, None) == -2
+    assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 64, big, 8192, 0, 1, None, 0, None) == -2
+    assert fp4.fp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, None, None, None, 0, FAKE, None, big, 64, 8192, 0, 1,
+                           None) == -2
+    assert fp4.fp4_gemm_grouped(FAKE, FAKE, big, FAKE, FAKE, 4, FAKE, FAKE, None, None, FAKE, 64, 64, 8192, 0, 1,
+                                None, 0, None) == -2
