@@ -53,29 +53,33 @@ __device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
 // the last workgroup to finish turns the maximum into s_t = amax / (6 * 448),
 // writes it, and clears the two workspace words for the next call.
 // ---------------------------------------------------------------------------
-// Each workgroup pass covers a 16 KB span: every lane issues four 16-byte
-// loads (a wave's load reads 1 KB contiguous) before it folds any of them, so
-// that 4 KB per wave are in flight; buffer loads bound the last, partial span
-// without a branch.  The max runs on the magnitude bits (for finite values
-// the integer order is the order of |x|).  A dword holds one FP32 value or
-// two BF16 values (each the high half of an FP32 value).
-constexpr uint32_t kAmaxSpan = 16384u;
-
-template <int DT>
-__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, size_t nbytes,
+// Each workgroup pass covers a span of TPB * NL * 16 bytes: every lane
+// issues NL 16-byte loads (a wave's load reads 1 KB contiguous) before it
+// folds any of them; buffer loads bound the last, partial span without a
+// branch.  The max runs on the magnitude bits (for finite values the integer
+// order is the order of |x|).  A dword holds one FP32 value or two BF16
+// values (each the high half of an FP32 value).
+//
+// The grid is small (at most 128 workgroups): the completion protocol below
+// costs two device-scope atomics per workgroup on one address, and those
+// serialise (measured ~9.5 ns each: 2048 workgroups added ~38 us to an
+// otherwise 20 us pass over 134 MB).
+template <int DT, int TPB, int NL>
+__global__ __launch_bounds__(TPB) void tensor_amax_kernel(const void* __restrict__ x, size_t nbytes,
                                                           uint32_t* __restrict__ ws, float* __restrict__ ts) {
+  constexpr uint32_t SPAN = (uint32_t)TPB * 16u * (uint32_t)NL;
   uint32_t mb = 0u;
-  const size_t step = (size_t)gridDim.x * kAmaxSpan;
-  for (size_t off = (size_t)blockIdx.x * kAmaxSpan; off < nbytes; off += step) {
+  const size_t step = (size_t)gridDim.x * SPAN;
+  for (size_t off = (size_t)blockIdx.x * SPAN; off < nbytes; off += step) {
     const size_t rem = nbytes - off;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(static_cast<const uint8_t*>(x) + off, rem < kAmaxSpan ? (uint32_t)rem : kAmaxSpan);
-    u32x4 w[4];
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<const uint8_t*>(x) + off, rem < SPAN ? (uint32_t)rem : SPAN);
+    u32x4 w[NL];
 #pragma unroll
-    for (uint32_t u = 0; u < 4u; ++u)
-      w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256u + threadIdx.x) * 16u, 0, 0));
+    for (uint32_t u = 0; u < (uint32_t)NL; ++u)
+      w[u] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (u * (uint32_t)TPB + threadIdx.x) * 16u, 0, 0));
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NL; ++u)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (DT == kDtF32) {
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
   float m = u2f(mb);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float red[4];
+  __shared__ float red[TPB / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -98,7 +102,8 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
     // return before the add; the block that counts last then reads the final
     // max.  (A release fence here would write back and invalidate the XCD's
     // whole L2 once per block.)
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+    for (int i = 1; i < TPB / 64; ++i) m = fmaxf(m, red[i]);
     const uint32_t prev = __hip_atomic_fetch_max(&ws[0], f2u(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" : : "v"(prev) : "memory");
     const uint32_t done = __hip_atomic_fetch_add(&ws[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -539,13 +544,26 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* ws, float* tensor_scale,
                               hipStream_t stream) {
   const size_t nbytes = (size_t)n * (in_dtype == kDtF32 ? 4u : 2u);
-  size_t blocks = (nbytes + kAmaxSpan - 1) / kAmaxSpan;
-  if (blocks > 2048) blocks = 2048;   // 8 workgroups of 4 waves per compute unit
+  // Measured (8192^2 BF16 = 134 MB: 21.8 us; 33.5 MB: 7.6 us; 4 MB: 4.7 us):
+  // up to 8 MB, 256-thread workgroups with 32 KB spans, at most 64 of them;
+  // beyond, 1024-thread workgroups with 64 KB spans, at most 128.
+  const bool big = nbytes > (size_t(8) << 20);
+  const size_t span = big ? 65536u : 32768u, cap = big ? 128u : 64u;
+  size_t blocks = (nbytes + span - 1) / span;
+  if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  if (in_dtype == kDtF32)
-    tensor_amax_kernel<kDtF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
-  else
-    tensor_amax_kernel<kDtBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
+  const dim3 grid((unsigned)blocks);
+  if (in_dtype == kDtF32) {
+    if (big)
+      tensor_amax_kernel<kDtF32, 1024, 4><<<grid, dim3(1024), 0, stream>>>(x, nbytes, ws, tensor_scale);
+    else
+      tensor_amax_kernel<kDtF32, 256, 8><<<grid, dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
+  } else {
+    if (big)
+      tensor_amax_kernel<kDtBF16, 1024, 4><<<grid, dim3(1024), 0, stream>>>(x, nbytes, ws, tensor_scale);
+    else
+      tensor_amax_kernel<kDtBF16, 256, 8><<<grid, dim3(256), 0, stream>>>(x, nbytes, ws, tensor_scale);
+  }
   return hipGetLastError();
 }
 
