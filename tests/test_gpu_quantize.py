@@ -118,3 +118,12 @@ def test_full_size_operands_bit_exact(orc):
     _run(orc, 0, a)
     _, w = synth.nvfp4_mlp()
     _run(orc, 1, w)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
+def test_large_bf16_multi_item_path(orc, fmt):
+    """BF16 inputs large enough (at least 32768 row slices of 512 values) for
+    the quantisers to give each wave four slices: 4100 x 4000 (padding rows
+    and a ragged last slice), with edge values; bit-exact, all formats."""
+    x = synth.to_bf16_bits(_special(4100, 4000, 97 + fmt))
+    _run(orc, fmt, x)
