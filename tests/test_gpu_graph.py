@@ -123,3 +123,42 @@ def test_graph_mxfp4_small(orc):
     g = _capture(step, 2)
     other = torch.randn(256, 256, device="cuda")
     _replay_and_check(g, C, ref, lambda: fp4.gemm(fp4.quantize(other, fp4.MXFP4), qb))
+
+
+def test_graph_w4a8_step(orc):
+    """BF16 activations -> MXFP8, times MXFP4 weights (fp4_gemm_w4a8) with
+    bias and ReLU, captured twice in one graph; every replay equals the eager
+    result, which is checked against the oracle's exact values (grid data:
+    every product fits the matrix core's window and every sum is exact)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    M, N, K = 96, 320, 512
+    g = synth.rng(71)
+    a = ((g.integers(0, 16, (M, K)) * 0.25) * np.where(g.random((M, K)) < 0.5, -1, 1)).astype(np.float32)
+    a[:, ::32] = 3.75
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    w = (grid[g.integers(0, 8, (N, K))] * np.where(g.random((N, K)) < 0.5, -1, 1)).astype(np.float32)
+    w[:, ::32] = 6.0
+    bias = (g.integers(-64, 64, N) * 0.25).astype(np.float32)
+    say("graph w4a8")
+    xa = to_dev(synth.to_bf16_bits(a))
+    qw = fp4.quantize(to_dev(w), fp4.MXFP4)
+    qa = fp4.quantize(xa, fp4.MXFP8)
+    bd = to_dev(bias)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp4.quantize(xa, fp4.MXFP8, out=qa)
+        fp4.gemm_w4a8(qa, qw, bias=bd, act=fp4.ACT_RELU, out=C)
+
+    step()
+    torch.cuda.synchronize()
+    ref = C.clone()
+    ra = orc.quantize(synth.to_bf16_bits(a), orc.FMT_MXFP8)
+    rw = orc.quantize(w, orc.FMT_MXFP4)
+    Cref, _ = orc.gemm_mixed(ra[0], ra[1], orc.FMT_MXFP8, rw[0], rw[1], orc.FMT_MXFP4, M, N, K)
+    np.testing.assert_array_equal(to_host(C), orc.epilogue(Cref, bias, orc.ACT_RELU))
+
+    gr = _capture(step, 2)
+    other = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    _replay_and_check(gr, C, ref, lambda: fp4.gemm_w4a8(fp4.quantize(other, fp4.MXFP8), qw))
