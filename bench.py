@@ -15,9 +15,9 @@ workload, and, under "workloads", the other measured workloads:
 
   nvfp4_decode_m{1,8,32}  W 8192x8192 NVFP4 (pre-quantised), X Mx8192 BF16
                           quantised on the fly; step = tensor amax + quantise
-                          + decode GEMV (one fused kernel at M = 1, three
-                          kernels at M = 8, 32); GB/s of algorithmic bytes vs
-                          8 TB/s.
+                          + decode GEMV (one fused kernel at M = 1, two
+                          kernels at M = 8, three at M = 32); GB/s of
+                          algorithmic bytes vs 8 TB/s.
   nvfp4_mlp               A 4096x4096 BF16 quantised on the fly, W 14336x4096
                           NVFP4; step = amax + quantise + GEMM; TFLOP/s.
   mxfp4_moe               32 experts 5760x2880 MXFP4, 16384 BF16 tokens
@@ -319,6 +319,7 @@ def nvfp4_decode(torch, fp4, synth, M):
     # three-kernel step at small M only (measured: M = 1 16.3 vs 18.4 us,
     # M = 8 22.3 vs 21.3 us).
     fused = M <= 4 and bool(fp4.fp4_gemm_nvfp4_act_supported(M, N, K, fp4.BF16))
+    small_x = M * K * 2 <= 256 * 1024   # fp4_quantize's one-launch NVFP4 path (tensors up to 256 KB)
     if fused:
         # one kernel: tensor amax + NVFP4 quantise of X + GEMV
         def step(i):
@@ -348,7 +349,8 @@ def nvfp4_decode(torch, fp4, synth, M):
     return {"M": M, "N": N, "K": K, "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": int(nbytes),
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "step": ("one kernel: tensor amax + NVFP4 quantise of X + decode GEMV" if fused else
-                     "three kernels: tensor amax, NVFP4 quantise of X, decode GEMV") + " (HIP graph replay)"}
+                     ("two kernels: one-launch tensor amax + NVFP4 quantise of X, decode GEMV" if small_x else
+                      "three kernels: tensor amax, NVFP4 quantise of X, decode GEMV")) + " (HIP graph replay)"}
 
 
 def nvfp4_mlp(torch, fp4, synth):
