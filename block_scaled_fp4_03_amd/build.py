@@ -17,7 +17,7 @@ OUT = os.path.join(HERE, "libfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "quantize.hip", "gemm.hip", "gemm_w4a8.hip", "gemv_nv.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "gemm.hip", "gemm_w4a8.hip", "gemv_nv.hip", "gemv_nv_blocksum.hip"]
 
 # -ffp-contract=off: no silent a*b+c fusion (the quantiser must round exactly
 # like the IEEE definition).  The packed-FP32 feature is switched off for the

@@ -39,7 +39,7 @@ def _case(orc, M, N, K, x, w, out_bf16, given_ts=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (2, 64, 288), (4, 257, 8192),
-                                   (32, 70, 1024)])
+                                   (32, 70, 1024), (1, 64, 17440), (6, 96, 800), (8, 64, 8192), (12, 64, 512)])
 @pytest.mark.parametrize("bf16_x", [True, False])
 def test_fused_decode_matches_oracle(orc, M, N, K, bf16_x):
     x = synth.gaussian(300 + M, (M, K), every=97)

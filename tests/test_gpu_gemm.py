@@ -157,13 +157,14 @@ def test_closed_forms_bit_exact(orc, fmt):
         np.testing.assert_array_equal(C, ref)
 
 
-@pytest.mark.parametrize("M", [5, 20, 40])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 20, 40])
 def test_nvfp4_every_e4m3_scale_byte(orc, M):
     """Every finite E4M3 byte as a block scale of A and of B, exactly: W row n
     holds 1.0 codes only in block n, with scale byte n; A row m holds 1.0 codes
     with scale byte (7m + 13b) mod 127 in block b; so C[m, n] = 16 * e4m3(sA) *
-    e4m3(n), a product exact in FP32.  M = 5 and 20 take the decode kernel's two
-    activation stagings, M = 40 the tiled GEMM."""
+    e4m3(n), a product exact in FP32.  M = 1, 2, 3, 5 take the block-sum decode
+    kernel (1, 2, 4 and 8 activation rows per operand), M = 20 the FP16 decode
+    kernel, M = 40 the tiled GEMM."""
     fmt, N, K = 1, 127, 2048
     A = np.full((M, K), 2, np.uint8)
     B = np.zeros((N, K), np.uint8)
@@ -251,6 +252,16 @@ def test_nvfp4_decode_gemv(orc, M, N, K, bf16_out):
     """M <= 32 rows take the decode kernel (K split over the workgroup's
     waves, reduced in LDS); checked in full against the oracle."""
     _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 13 + N + K, a_std=1.0, b_std=0.02)
+
+
+# The block-sum decode kernel (M <= 8): every operand packing (M = 1, 2,
+# 3-4, 5-8), K tails that end inside a 512-value unit and inside a 256-value
+# scale tile (K = 96, 288, 800, 4128), several units per wave (K = 17440 at
+# M = 1: 35 units; 12320 at M = 2: 25 units), ragged N.
+@pytest.mark.parametrize("M,N,K", [(1, 200, 17440), (2, 130, 12320), (4, 96, 4128), (5, 64, 800), (6, 300, 96),
+                                   (7, 40, 288), (8, 257, 8192)])
+def test_nvfp4_decode_blocksum_shapes(orc, M, N, K):
+    _gemm_case(orc, 1, M, N, K, False, seed=M * 7 + N + K, a_std=1.0, b_std=0.02)
 
 
 def test_nvfp4_decode_gemv_repeated_calls(orc):
