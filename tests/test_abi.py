@@ -172,7 +172,9 @@ def test_fused_decode_supported_shapes(L):
     assert s(8, 8192, 8192, fp4.BF16) == 1
     assert s(16, 8192, 8192, fp4.BF16) == 0
     assert s(4, 8192, 8192, fp4.F32) == 1
-    assert s(8, 8192, 8192, fp4.F32) == 0
+    assert s(8, 8192, 8192, fp4.F32) == 1     # M <= 8: the block-sum decode kernel stages up to 4096 blocks
+    assert s(8, 64, 8704, fp4.F32) == 0       # 4352 blocks: neither decode kernel's staging holds them
+    assert s(1, 64, 32768, fp4.BF16) == 1
     assert s(32, 64, 1024, fp4.BF16) == 1
     assert s(33, 64, 1024, fp4.BF16) == 0
     assert s(1, 64, 48, fp4.BF16) == 0  # K % 32
