@@ -316,9 +316,9 @@ def nvfp4_decode(torch, fp4, synth, M):
     x = to_dev(torch, synth.nvfp4_decode_act(M))
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     # The one-kernel path re-quantises X in every workgroup; it beats the
-    # three-kernel step at small M only (measured: M = 1 16.3 vs 18.4 us,
-    # M = 8 22.3 vs 21.3 us).
-    fused = M <= 4 and bool(fp4.fp4_gemm_nvfp4_act_supported(M, N, K, fp4.BF16))
+    # quantise + GEMM step at small M only (measured: M = 1 11.6 vs 14.3 us,
+    # M = 2 12.4 vs 14.0 us, M = 4 16.9 vs 14.6 us).
+    fused = M <= 2 and bool(fp4.fp4_gemm_nvfp4_act_supported(M, N, K, fp4.BF16))
     small_x = M * K * 2 <= 256 * 1024   # fp4_quantize's one-launch NVFP4 path (tensors up to 256 KB)
     if fused:
         # one kernel: tensor amax + NVFP4 quantise of X + GEMV
