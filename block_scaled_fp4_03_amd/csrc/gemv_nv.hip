@@ -247,8 +247,7 @@ __global__ __launch_bounds__(GV_WAVES * 64, 1) void gemv_nv_kernel(
       for (int i = 0; i < XNB; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(xv[i][e]));
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      m = wave_fmax(m);
       if (lane == 0) red[0][0][wave] = m;
       __syncthreads();
       float amax = 0.0f;

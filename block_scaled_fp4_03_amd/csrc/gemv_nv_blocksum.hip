@@ -55,26 +55,6 @@ namespace {
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-// The value of the adjacent lane (lanes 2i and 2i + 1 swap: DPP quad_perm
-// [1, 0, 3, 2]).
-__device__ __forceinline__ float pair_other(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-}
-
-// Largest of non-negative values over the wavefront (such floats order as
-// their bit patterns): rotations by 1, 2, 4, 8 within each row of 16 lanes
-// (DPP row_ror), then the four rows' results.
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  int x = __builtin_bit_cast(int, v);
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x121, 0xF, 0xF, false));
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x122, 0xF, 0xF, false));
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false));
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
-  const int r = max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-                    max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-  return __builtin_bit_cast(float, r);
-}
-
 constexpr uint32_t BS_WAVES = 16;
 constexpr uint32_t BS_LDS_BYTES = 160u * 1024u;
 // Weight steps requested before the activation is staged (4 of 8).
@@ -248,7 +228,7 @@ __global__ __launch_bounds__(BS_WAVES * 64, 1) void gemv_bs_kernel(
       float a = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(xv[i][e]));
-      am[i] = fmaxf(a, pair_other(a));
+      am[i] = fmaxf(a, lane_xor1(a));
     }
     // Tensor scale (NVFP4 video transcript: one FP32 scale for the global
     // range): amax / (6 * 448), 1 for an all-zero X, at least FLT_MIN; or the
@@ -259,7 +239,7 @@ __global__ __launch_bounds__(BS_WAVES * 64, 1) void gemv_bs_kernel(
       float mx = 0.0f;
 #pragma unroll
       for (int i = 0; i < NX; ++i) mx = fmaxf(mx, am[i]);
-      mx = wave_max_nonneg(mx);
+      mx = wave_fmax(mx);
       if (lane == 0) red[wave] = mx;
       __syncthreads();
       float amax = 0.0f;

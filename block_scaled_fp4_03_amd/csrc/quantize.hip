@@ -91,8 +91,7 @@ __global__ __launch_bounds__(TPB) void tensor_amax_kernel(const void* __restrict
       }
   }
   float m = u2f(mb);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = wave_fmax(m);
   __shared__ float red[TPB / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -143,8 +142,8 @@ __device__ __forceinline__ void quantize_mx_item(const float (&v)[8], bool valid
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, lane_xor1(am));
+  am = fmaxf(am, lane_xor2(am));
   constexpr bool FP8 = FMT == kFmtMX8 || FMT == kFmtMX8Ocp;
   static_assert(!(FP8 && SR), "stochastic rounding is defined for E2M1 only");
   const uint32_t sbyte = FP8 ? mx8_scale_byte<FMT>(am) : mx_scale_byte<FMT>(am);  // 0 for padding (am == 0)
@@ -256,7 +255,7 @@ __device__ __forceinline__ void quantize_nv_wave(const float v[8], bool valid, u
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
-  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, lane_xor1(am));
   if (am_in >= 0.0f) am = am_in;
   const float r = (am / 6.0f) / s_t;
   const uint32_t sb = e4m3_encode(r);
@@ -385,8 +384,7 @@ __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __r
           }
         }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = wave_fmax(m);
   if (lane == 0u) red[w] = m;
   __syncthreads();
   float amax = red[0];
@@ -435,7 +433,7 @@ __global__ __launch_bounds__(1024) void quantize_nv2d_kernel(const void* __restr
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
-  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, lane_xor1(am));
   if ((lane & 1u) == 0u) blk[w][lane >> 1] = am;
   __syncthreads();
   float pm = 0.0f;
@@ -487,7 +485,7 @@ __global__ __launch_bounds__(256) void hadamard16_kernel(const void* __restrict_
     const bool upper = (lane & 1u) != 0u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float o = __shfl_xor(v[k], 1);
+      const float o = lane_xor1(v[k]);
       v[k] = upper ? o - v[k] : v[k] + o;
     }
 #pragma unroll

@@ -4,7 +4,7 @@ A^[m, n] (B identity) or B^[n, m] (A identity), each value times the scales
 of its K block.  Every K position of a 512-value K (both halves of each
 64-value step, both 256-value scale tiles), every scale block and both
 operands' scale-lane mappings are checked bit for bit, for MXFP4, NVFP4 (tiled
-kernel and, at M <= 32, the decode kernel) and W4A8 ("Rubin FP4 GEMM deep
+kernel and, at M <= 32, both decode kernels) and W4A8 ("Rubin FP4 GEMM deep
 dive" §5.2: nibble order and scale layout must match what the kernel reads)."""
 import numpy as np
 import pytest
@@ -77,10 +77,11 @@ def test_identity_a_pins_b_layout(orc, fmt):
     np.testing.assert_array_equal(C, want)
 
 
-@pytest.mark.parametrize("fmt,M", [(0, 40), (1, 40), (1, 8), (1, 32)])
+@pytest.mark.parametrize("fmt,M", [(0, 40), (1, 40), (1, 1), (1, 2), (1, 3), (1, 8), (1, 32)])
 def test_identity_b_pins_a_layout(orc, fmt, M):
     """B = identity (512 x 512), A random: C[m, n] = A^[m, n] * sB(n).  NVFP4
-    with M <= 32 takes the decode kernel (both of its activation stagings)."""
+    with M <= 8 takes the block-sum decode kernel (M = 1, 2, 3, 8: one, two,
+    four and eight activation rows per operand), M = 32 the FP16-decode kernel."""
     N = K
     g = np.random.default_rng(32 + M)
     ra, rb = _scale_rules(fmt)
