@@ -241,15 +241,18 @@ def test_nvfp4_mlp_sampled(orc):
     assert_gemm_close(orc, Cs, Cref, T, True, "nvfp4_mlp sampled")
 
 
-# Activation staged as FP16 (M x K small), as codes (larger), or too large for
-# the decode kernel (the tiled GEMM takes it): (8, 100, 8960) is the largest
-# FP16 staging at M = 8, (32, 130, 8192) the largest code staging.
+# M <= 8 within its K reach takes the block-sum decode kernel; otherwise the
+# FP16-decode kernel stages the activation as FP16 (M x K small), as codes
+# (larger), or it is too large for either (the tiled GEMM takes it):
+# (8, 100, 8960) is the largest FP16 staging at M = 8 (past the block-sum
+# kernel's K = 8192 at M = 8), (32, 130, 8192) the largest code staging,
+# (2, 64, 40000) small M past both decode kernels' K reach.
 @pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (17, 256, 4096), (32, 130, 8192),
                                    (1, 8192, 256), (32, 64, 96), (8, 100, 8960), (9, 100, 8192), (32, 64, 8448),
                                    (2, 64, 40000)])
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_nvfp4_decode_gemv(orc, M, N, K, bf16_out):
-    """M <= 32 rows take the decode kernel (K split over the workgroup's
+    """M <= 32 rows take a decode kernel (K split over the workgroup's
     waves, reduced in LDS); checked in full against the oracle."""
     _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 13 + N + K, a_std=1.0, b_std=0.02)
 

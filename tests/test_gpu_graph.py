@@ -1,8 +1,8 @@
 """Quantise + GEMM steps captured in a HIP graph: every replay (with eager work
 and synchronisations in between) must reproduce the eager result bit for bit,
-and the eager result must agree with the oracle.  The NVFP4 step includes the
-tensor-amax reduction and the decode GEMV, both of which keep self-resetting
-counters in the workspace, so a replay that saw stale counters would differ."""
+and the eager result must agree with the oracle.  The NVFP4 steps include the
+tensor-amax reduction, which keeps a self-resetting counter in the workspace,
+so a replay that saw a stale counter would differ."""
 import numpy as np
 import pytest
 
