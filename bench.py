@@ -10,8 +10,11 @@ steps are not served from the 256 MB Infinity Cache.  Before each workload's
 warm-up its step runs untimed for --settle seconds (default 0.25) so that the
 GPU's clocks have reached their sustained level under load.  The same line carries
 the dominant kernel's roofline (HIP events around the timed launches, on the
-launch stream), the CPU oracle timed on a bounded sample of the same
-workload, and, under "workloads", the other measured workloads:
+launch stream), the GPU's shader clock and socket power sampled while the
+headline ran ("gpu_telemetry": the chip runs at its power cap under this
+load, so the clock it settles to bounds the matrix-core rate), the CPU oracle
+timed on a bounded sample of the same workload, and, under "workloads", the
+other measured workloads:
 
   nvfp4_decode_m{1,8,32}  W 8192x8192 NVFP4 (pre-quantised), X Mx8192 BF16
                           quantised on the fly; step = tensor amax + quantise
@@ -47,6 +50,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -85,6 +89,69 @@ def arithmetic_intensity(M, N, K, block=32, out_bytes=2, include_c=True):
 
 # ---- timing helpers ---------------------------------------------------------
 SETTLE_S = 0.25
+
+
+class Telemetry:
+    """GFX clock (MHz) and socket power (W) sampled every 10 ms on a host
+    thread while a workload runs, through amdsmi (the driver's metrics).  The
+    readings lag the load by a few hundred milliseconds, so samples from the
+    first `skip_s` seconds are dropped.  summary() is None when amdsmi is
+    missing or cannot reach the GPU."""
+
+    def __init__(self, skip_s=1.0):
+        self.clk, self.pwr, self.cap, self.err = [], [], None, None
+        self.skip_s = skip_s
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_info(self._h).get("power_limit")
+            self.cap = cap / 1e6 if isinstance(cap, (int, float)) and cap > 1e4 else cap
+        except Exception as e:  # no amdsmi, no driver access: telemetry is optional
+            self._smi, self.err = None, "%s: %s" % (type(e).__name__, e)
+
+    def _run(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            if time.perf_counter() - t0 < self.skip_s:
+                time.sleep(0.01)
+                continue
+            try:
+                c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX).get("clk")
+                p = self._smi.amdsmi_get_power_info(self._h).get("current_socket_power")
+                if isinstance(c, (int, float)):
+                    self.clk.append(float(c))
+                if isinstance(p, (int, float)):
+                    self.pwr.append(float(p))
+            except Exception as e:
+                self.err = "%s: %s" % (type(e).__name__, e)
+                return
+            time.sleep(0.01)
+
+    def __enter__(self):
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self, what):
+        if self._smi is None or not self.clk:
+            return None if self.err is None else {"error": self.err}
+
+        def stats(v):
+            v = sorted(v)
+            return {"median": v[len(v) // 2], "p10": v[len(v) // 10], "p90": v[(len(v) * 9) // 10]} if v else None
+        return {"during": what, "source": "amdsmi", "samples": len(self.clk), "gfxclk_mhz": stats(self.clk),
+                "socket_power_w": stats(self.pwr), "power_cap_w": self.cap}
 
 
 def time_steps(torch, step, steps, warmup):
@@ -175,7 +242,18 @@ def mxfp4_gemm_8192(torch, fp4, synth, args):
 
     ms = time_steps(torch, step, args.steps, args.warmup)
     tflops = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
-    return dict(ms=ms, tflops=tflops, a=a, b=b)
+    # Clock and power under the same load: 2.5 s of the same steps after the
+    # timed ones (the driver's readings need longer than the timed region).
+    with Telemetry() as tel:
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 2.5:
+            step(i)
+            i += 1
+            if i % 32 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    return dict(ms=ms, tflops=tflops, a=a, b=b,
+                telemetry=tel.summary("2.5 s of headline steps right after the timed ones (first 1 s dropped)"))
 
 
 def mxfp4_gemm_requant_8192(torch, fp4, synth, a, b):
@@ -527,6 +605,7 @@ def main():
                      "kernel": "gemm_kernel<MXFP4, BF16, dense>",
                      "algorithmic_flops_per_launch": gemm_flops(8192, 8192, 8192)},
         "cpu_baseline": cpu,
+        "gpu_telemetry": head["telemetry"],
         "workloads": extra,
         "wall_s": round(time.perf_counter() - t_start, 1),
     }
