@@ -236,6 +236,21 @@ __device__ __forceinline__ v8h decode8(uint32_t w, v2h s) {
 // "Parallel random numbers: as easy as 1, 2, 3", SC 2011), ten rounds of
 // two 64 x 64 -> 128-bit products mixed with the key, the key advanced by
 // two Weyl constants between rounds.
+//
+// The 128-bit product of two 64-bit words, schoolbook from four 32 x 32 -> 64
+// partial products (each one v_mad_u64_u32, the carries folded into the
+// addends: no sum below can exceed 2^64 - 1).  Computing the low half with a
+// plain 64-bit multiply and the high half with __umul64hi repeats partial
+// products, and the multiplies are what bound the stochastic quantiser.
+__device__ __forceinline__ void mul_wide_u64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32), b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t t = (uint64_t)a0 * b1 + (p00 >> 32);
+  const uint64_t u = (uint64_t)a1 * b0 + (uint32_t)t;
+  lo = (u << 32) | (uint32_t)p00;
+  hi = (uint64_t)a1 * b1 + ((t >> 32) + (u >> 32));
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
@@ -245,8 +260,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uin
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_wide_u64(M0, c[0], hi0, lo0);
+    mul_wide_u64(M1, c[2], hi1, lo1);
     const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
