@@ -40,6 +40,16 @@ def test_hadamard_bf16_out_and_in_place(orc):
     np.testing.assert_array_equal(to_host(x32), orc.rht16(synth.gaussian(8, (64, 2048)), 5))
 
 
+def test_hadamard_full_size_8192(orc):
+    """The Hadamard workload the benchmark times: 8192 x 8192 BF16 N(0, 1)
+    through the BF16 -> BF16 launch, one of its seeds: bit-exact."""
+    import block_scaled_fp4_03_amd as fp4
+    x = synth.to_bf16_bits(synth.gaussian(82, (8192, 8192)))
+    say("hadamard16 8192^2 bf16 -> bf16 seed 3")
+    y = fp4.hadamard16(to_dev(x), seed=3)
+    np.testing.assert_array_equal(to_host(y), orc.f32_to_bf16_bits(orc.rht16(x, 3)))
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_hadamard_then_quantise(orc, fmt):
     """Transform then quantise, as the recipe orders it: bit-exact."""
