@@ -637,7 +637,9 @@ void launch_q(const void* x, int fmt, int in_dtype, uint8_t* codes, uint8_t* sca
   // that still leaves eight waves per SIMD.  Measured: MXFP4 16384 x 2880 BF16
   // 27.4 -> 23.4 us, NVFP4 8192^2 BF16 43.0 -> 41.3 us; 8192^2 FP32 56.3 us
   // with one item, 59.5 with two, 61.8 with four; a 32 x 8192 decode
-  // activation (512 items) slower with four.  Stochastic rounding keeps one.
+  // activation (512 items) slower with four.  Stochastic rounding keeps one:
+  // its Philox multiplies bound it, and NVFP4 8192^2 BF16 took 160.7 us with
+  // one item, 162.5 with two, 162.0 with four.
   constexpr int IT = SR ? 1 : 4;
   const bool multi = waves >= 32768u;
   const dim3 gridm((waves + 4u * IT - 1u) / (4u * IT));
