@@ -295,9 +295,13 @@ def nvfp4_quantize_sr_8192(torch, fp4, synth):
     ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, n, 0, n)
     ms_sr = time_steps(torch, lambda i: fp4.quantize(x, fp4.NVFP4, ws=ws, out=q, sr_seed=i + 1), 30, 5)
     ms_rn = time_steps(torch, lambda i: fp4.quantize(x, fp4.NVFP4, ws=ws, out=q), 30, 5)
-    nbytes = 2 * n * n * 2 + n * n // 2 + n * n // 16      # input read twice (amax, quantise), codes, scales
+    # Algorithmic bytes: the input read once, codes and scales written once.
+    # The step reads the input twice (amax pass, then quantise pass); that
+    # second read is not credited.
+    nbytes = n * n * 2 + n * n // 2 + n * n // 16
     gbs = nbytes / (ms_sr * 1e-3) / 1e9
-    return {"us_per_step": round(ms_sr * 1e3, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+    return {"us_per_step": round(ms_sr * 1e3, 2), "algorithmic_bytes": int(nbytes), "GB_per_s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "passes_over_input": 2,
             "us_per_step_round_to_nearest": round(ms_rn * 1e3, 2),
             "step": "tensor amax + NVFP4 quantise with stochastic rounding (Philox4x64-10 per element)"}
 
@@ -326,10 +330,13 @@ def nvfp4_quantize_2d_weight(torch, fp4, synth):
     ms2 = time_steps(torch, lambda i: fp4.quantize(wd, fp4.NVFP4, ws=ws, out=q, two_d=True), 20, 3)
     ms1 = time_steps(torch, lambda i: fp4.quantize(wd, fp4.NVFP4, ws=ws, out=q), 20, 3)
     n = wd.numel()
-    nbytes = 2 * n * 4 + n // 2 + n // 16
+    # Input read once (the amax pass's second read is not credited), codes
+    # and scales written once.
+    nbytes = n * 4 + n // 2 + n // 16
     gbs = nbytes / (ms2 * 1e-3) / 1e9
     return {"rows": int(wd.shape[0]), "K": int(wd.shape[1]), "us_per_step": round(ms2 * 1e3, 2),
-            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": int(nbytes), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "passes_over_input": 2,
             "us_per_step_1x16": round(ms1 * 1e3, 2),
             "step": "tensor amax + NVFP4 quantise with one scale per 16 x 16 patch (FP32 in)"}
 
@@ -476,7 +483,11 @@ def mxfp4_moe(torch, fp4, synth):
     ms = time_steps(torch, step, 10, 2)
     tf = gemm_flops(total, N, K) / (ms * 1e-3) / 1e12
     nonempty = int((counts > 0).sum())
-    nbytes = (nonempty * fp4_operand_bytes(N, K, 32) + T * K * 2 + fp4_operand_bytes(T, K, 32) * 2 + total * N * 2)
+    # Algorithmic bytes: the non-empty experts' weights (codes + scales) and
+    # the BF16 tokens read once, C written once.  The quantised tokens are an
+    # intermediate (written by the quantiser, gathered by the GEMM) and are
+    # not credited.
+    nbytes = nonempty * fp4_operand_bytes(N, K, 32) + T * K * 2 + total * N * 2
     return {"experts": E, "N": N, "K": K, "tokens": T, "routed_rows": total, "ms_per_step": round(ms, 4),
             "TFLOP_per_s": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
             "algorithmic_bytes": int(nbytes),

@@ -158,6 +158,56 @@ def _check(rc, where):
         raise Fp4Error(rc, where)
 
 
+def _need(t, name, dtypes=None, numel=None, device=None, ndim=None):
+    """Reject, before any library call, an argument the C ABI would misread:
+    not a tensor, not on a GPU, not contiguous (the kernels take a raw
+    pointer and assume the documented dense layout), of another dtype (an
+    int64 index read as int32 halves), too small, or on another device than
+    the call's first operand.  Returns t."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, %d needed" % (name, t.numel(), numel))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor, got device %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the call's operands on %s" % (name, t.device, device))
+    return t
+
+
+def _need_q(q, name, device=None):
+    """Check a Quantized operand: codes, scales (and the NVFP4 tensor scale)
+    contiguous uint8 / float32 GPU tensors of the sizes its format needs."""
+    if not isinstance(q, Quantized):
+        raise TypeError("%s must be a Quantized, got %s" % (name, type(q).__name__))
+    torch = _torch()
+    if q.fmt == NVFP4 and q.tensor_scale is None:
+        raise ValueError("%s: an NVFP4 operand needs its tensor scale" % name)
+    ncodes = q.rows * (q.K if is_fp8(q.fmt) else q.K // 2)
+    _need(q.codes, name + ".codes", (torch.uint8,), ncodes, device)
+    nbytes = fp4_scale_bytes(q.fmt, q.rows, q.K)
+    if nbytes < 0:
+        raise Fp4Error(int(nbytes), "fp4_scale_bytes")
+    _need(q.scales, name + ".scales", (torch.uint8,), nbytes, device)
+    if q.tensor_scale is not None:
+        _need(q.tensor_scale, name + ".tensor_scale", (torch.float32,), 1, device)
+    return q
+
+
+def _need_out(t, name, shape, dtypes, device):
+    _need(t, name, dtypes, None, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
 def _dtype_code(t):
     torch = _torch()
     if t.dtype == torch.float32:
@@ -196,8 +246,20 @@ def quantize(x, fmt, tensor_scale=None, ws=None, out=None, stream=None, sr_seed=
     round the elements stochastically with that seed (fp4_quantize_sr).
     two_d: NVFP4 scales per 16 x 16 patch (fp4_quantize_ex, FP4_Q_2D)."""
     torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16), ndim=2)
     rows, K = x.shape
     dev = x.device
+    if tensor_scale is not None:
+        _need(tensor_scale, "tensor_scale", (torch.float32,), 1, dev)
+    if ws is not None:
+        _need(ws, "ws", (torch.uint8,), None, dev)
+    if out is not None:
+        if (out.rows, out.K, out.fmt) != (rows, K, fmt):
+            raise ValueError("out is a %d x %d matrix of format %d, x needs %d x %d of format %d"
+                             % (out.rows, out.K, out.fmt, rows, K, fmt))
+        if fmt == NVFP4 and out.tensor_scale is None:
+            raise ValueError("out: an NVFP4 result needs a tensor-scale tensor")
+        _need_q(out, "out", dev)
     if out is None:
         codes = torch.empty((rows, K if is_fp8(fmt) else K // 2), dtype=torch.uint8, device=dev)
         nbytes = fp4_scale_bytes(fmt, rows, K)
@@ -231,9 +293,11 @@ def hadamard16(x, seed, out_dtype=None, out=None, stream=None):
     """Random Hadamard transform of a 2-D float32/bfloat16 CUDA tensor on
     16-value blocks along its last dimension (fp4_hadamard16)."""
     torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16), ndim=2)
     rows, K = x.shape
     if out is None:
         out = torch.empty((rows, K), dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    _need_out(out, "out", (rows, K), (torch.float32, torch.bfloat16), x.device)
     rc = fp4_hadamard16(_ptr(x), _dtype_code(x), _ptr(out), _dtype_code(out), rows, K, seed, _stream(stream))
     _check(rc, "fp4_hadamard16")
     return out
@@ -241,6 +305,7 @@ def hadamard16(x, seed, out_dtype=None, out=None, stream=None):
 
 def dequantize(q, out_dtype=None, stream=None):
     torch = _torch()
+    _need_q(q, "q")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     out = torch.empty((q.rows, q.K), dtype=out_dtype, device=q.codes.device)
     rc = fp4_dequantize(_ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), q.fmt, _ptr(out), _dtype_code(out),
@@ -252,13 +317,18 @@ def dequantize(q, out_dtype=None, stream=None):
 def gemm(a, b, out_dtype=None, out=None, ws=None, stream=None):
     """C = A . B^T for quantised A (M x K) and B (N x K) of the same format."""
     torch = _torch()
+    dev = _need_q(a, "a").codes.device
+    _need_q(b, "b", dev)
     M, N, K = a.rows, b.rows, a.K
     if b.K != K or a.fmt != b.fmt:
         raise ValueError("operands disagree on K or format")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=a.codes.device)
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=dev)
+    _need_out(out, "out", (M, N), (torch.float32, torch.bfloat16), dev)
     if ws is None:
-        ws = workspace(OP_GEMM, a.fmt, M, N, K, device=a.codes.device)
+        ws = workspace(OP_GEMM, a.fmt, M, N, K, device=dev)
+    else:
+        _need(ws, "ws", (torch.uint8,), None, dev)
     rc = fp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(a.tensor_scale),
                   _ptr(b.tensor_scale), _ptr(out), M, N, K, a.fmt, _dtype_code(out), _ptr(ws),
                   0 if ws is None else ws.numel(), _stream(stream))
@@ -273,10 +343,13 @@ def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
     bias: N float32 CUDA tensor or None.  C: optional preallocated output
     (tensor, or Quantized for FP4 output)."""
     torch = _torch()
+    dev = _need_q(a, "a").codes.device
+    _need_q(b, "b", dev)
     M, N, K = a.rows, b.rows, a.K
     if b.K != K or a.fmt != b.fmt:
         raise ValueError("operands disagree on K or format")
-    dev = a.codes.device
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), N, dev)
     fp4_out = out in (OUT_MXFP4, OUT_MXFP4_OCP)
     if C is None:
         if fp4_out:
@@ -288,6 +361,13 @@ def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
                           torch.empty(nbytes, dtype=torch.uint8, device=dev), None, ofmt, M, N)
         else:
             C = torch.empty((M, N), dtype=torch.float32 if out == OUT_F32 else torch.bfloat16, device=dev)
+    if fp4_out:
+        if (C.rows, C.K) != (M, N):
+            raise ValueError("C is a %d x %d matrix, the product %d x %d" % (C.rows, C.K, M, N))
+        _need(C.codes, "C.codes", (torch.uint8,), M * (N // 2), dev)
+        _need(C.scales, "C.scales", (torch.uint8,), max(0, fp4_scale_bytes(MXFP4, M, N)), dev)
+    else:
+        _need_out(C, "C", (M, N), (torch.float32 if out == OUT_F32 else torch.bfloat16,), dev)
     cptr, sptr = (_ptr(C.codes), _ptr(C.scales)) if fp4_out else (_ptr(C), None)
     rc = fp4_gemm_ex(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(a.tensor_scale),
                      _ptr(b.tensor_scale), _ptr(bias), act, cptr, sptr, M, N, K, a.fmt, out, _stream(stream))
@@ -299,11 +379,16 @@ def gemm_w4a8(a, b, bias=None, act=ACT_NONE, out_dtype=None, out=None, stream=No
     """C = act(A . B^T + bias) for MXFP8 activations A (M x K) and MXFP4
     weights B (N x K), FP32 accumulation (see fp4_gemm_w4a8 in include/fp4.h)."""
     torch = _torch()
+    dev = _need_q(a, "a").codes.device
+    _need_q(b, "b", dev)
     M, N, K = a.rows, b.rows, a.K
     if b.K != K or not is_fp8(a.fmt) or b.fmt not in (MXFP4, MXFP4_OCP):
         raise ValueError("A must be MXFP8 and B MXFP4 with the same K")
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), N, dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=a.codes.device)
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=dev)
+    _need_out(out, "out", (M, N), (torch.float32, torch.bfloat16), dev)
     rc = fp4_gemm_w4a8(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(bias), act, _ptr(out),
                        M, N, K, _dtype_code(out), _stream(stream))
     _check(rc, "fp4_gemm_w4a8")
@@ -314,13 +399,29 @@ def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_s
                  out=None, ws=None, stream=None):
     """Grouped (mixture-of-experts) GEMM; see fp4_gemm_grouped in include/fp4.h."""
     torch = _torch()
+    dev = _need_q(a, "a").codes.device
+    if a.K != K or a.fmt != fmt:
+        raise ValueError("a is %d x %d of format %d, the call K = %d, format %d" % (a.rows, a.K, a.fmt, K, fmt))
+    # int32 indices: torch's default int64 (cumsum, argsort) would be read as
+    # pairs of int32 halves.
+    _need(row_idx, "row_idx", (torch.int32,), None, dev, ndim=1)
+    _need(group_off, "group_off", (torch.int32,), 1, dev, ndim=1)
     E = group_off.numel() - 1
     total = row_idx.numel()
+    nscale = fp4_scale_bytes(fmt, N, K)
+    if nscale < 0:
+        raise Fp4Error(int(nscale), "fp4_scale_bytes")
+    _need(b_codes, "b_codes", (torch.uint8,), E * N * (K // 2), dev)
+    _need(b_scales, "b_scales", (torch.uint8,), E * nscale, dev)
+    if b_tensor_scale is not None:
+        _need(b_tensor_scale, "b_tensor_scale", (torch.float32,), 1, dev)
     if out is None:
-        out = torch.empty((total, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype,
-                          device=a.codes.device)
+        out = torch.empty((total, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=dev)
+    _need_out(out, "out", (total, N), (torch.float32, torch.bfloat16), dev)
     if ws is None:
-        ws = workspace(OP_GEMM_GROUPED, fmt, total, N, K, E, device=a.codes.device)
+        ws = workspace(OP_GEMM_GROUPED, fmt, total, N, K, E, device=dev)
+    else:
+        _need(ws, "ws", (torch.uint8,), None, dev)
     rc = fp4_gemm_grouped(_ptr(a.codes), _ptr(a.scales), a.rows, _ptr(row_idx), _ptr(group_off), E, _ptr(b_codes),
                           _ptr(b_scales), _ptr(a.tensor_scale), _ptr(b_tensor_scale), _ptr(out), total, N, K, fmt,
                           _dtype_code(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
@@ -334,12 +435,18 @@ def gemm_nvfp4_act(x, w, tensor_scale=None, ts_out=None, out_dtype=None, out=Non
     tensor_scale: given activation tensor scale (1-element float32 tensor), or
     None to compute it; ts_out: optional 1-element tensor receiving it."""
     torch = _torch()
+    _need(x, "x", (torch.float32, torch.bfloat16), ndim=2)
+    _need_q(w, "w", x.device)
     M, K = x.shape
     N = w.rows
     if w.K != K or w.fmt != NVFP4:
         raise ValueError("weights must be NVFP4 with the same K")
+    for t, name in ((tensor_scale, "tensor_scale"), (ts_out, "ts_out")):
+        if t is not None:
+            _need(t, name, (torch.float32,), 1, x.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=x.device)
+    _need_out(out, "out", (M, N), (torch.float32, torch.bfloat16), x.device)
     flags = TS_GIVEN if tensor_scale is not None else 0
     ts = tensor_scale if tensor_scale is not None else ts_out
     rc = fp4_gemm_nvfp4_act(_ptr(x), _dtype_code(x), _ptr(ts), flags, _ptr(w.codes), _ptr(w.scales),

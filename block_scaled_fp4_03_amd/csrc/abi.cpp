@@ -23,6 +23,17 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // Sizes are kept within what the kernels index with 32-bit arithmetic.
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// A launch's work-items per grid dimension are a 32-bit count, and the
+// element-wise kernels form their wave and thread indices from it in 32
+// bits.  The quantisers run one 64-lane wave per (row, 512-value slice) over
+// 32 * ceil(rows / 32) rows; dequantisation one thread per 8 values.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+bool quantize_grid_fits(int64_t rows, int64_t K) {
+  const int64_t rows_pad = (rows + 31) / 32 * 32, slices = (K + 511) / 512;
+  return rows_pad * slices * 64 <= kMaxWorkItems;
+}
+bool dequantize_grid_fits(int64_t rows, int64_t K) { return rows * (K / 8) + 255 <= kMaxWorkItems; }
 // A 256-row operand tile must stay within one 32-bit buffer range.
 constexpr int64_t kMaxGemmK = int64_t(1) << 24;
 
@@ -69,7 +80,7 @@ static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_
   if ((flags & FP4_Q_SR) && is_mx8(fmt)) return FP4_ERR_FMT;
   const bool sr = (flags & FP4_Q_SR) != 0u, twod = (flags & FP4_Q_2D) != 0u;
   if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
-  if (rows * K > (int64_t(1) << 40)) return FP4_ERR_SHAPE;
+  if (!quantize_grid_fits(rows, K)) return FP4_ERR_SHAPE;
   if (rows == 0 || K == 0) return FP4_OK;
   if (!x || !codes || !block_scales) return FP4_ERR_NULL;
   const bool nv = fmt == FP4_NVFP4;
@@ -132,7 +143,7 @@ int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const floa
   if (!qfmt_ok(fmt)) return FP4_ERR_FMT;
   if (!dtype_ok(out_dtype)) return FP4_ERR_DTYPE;
   if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
-  if (rows * K > (int64_t(1) << 40)) return FP4_ERR_SHAPE;
+  if (!dequantize_grid_fits(rows, K)) return FP4_ERR_SHAPE;
   if (rows == 0 || K == 0) return FP4_OK;
   if (!codes || !block_scales || !out) return FP4_ERR_NULL;
   if (fmt == FP4_NVFP4 && !tensor_scale) return FP4_ERR_NULL;

@@ -137,14 +137,27 @@ struct Groups {
   size_t b_scales_stride;    // bytes between experts' scale buffers
 };
 
+// Rows [lo, hi) of expert e, clamped so that 0 <= lo <= hi <= total: a
+// malformed group_off (negative, decreasing or past the end) can then only
+// drop rows, never address rows of C past the end.
+__device__ __forceinline__ void group_rows(const Groups& gp, int32_t e, uint32_t total, uint32_t& lo,
+                                           uint32_t& hi) {
+  const int32_t a = gp.group_off[e], b = gp.group_off[e + 1];
+  lo = a < 0 ? 0u : ((uint32_t)a < total ? (uint32_t)a : total);
+  hi = b < 0 ? 0u : ((uint32_t)b < total ? (uint32_t)b : total);
+  if (hi < lo) hi = lo;
+}
+
 // Locate tile t in the grouped list: tiles of expert e are ceil(cnt_e / BM)
 // m-tiles x tilesN n-tiles, ordered expert by expert.  Returns false past the
 // last tile.  Uniform per workgroup (scalar loads of group_off).
-__device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t t, uint32_t tilesN, uint32_t& e_out,
-                                             uint32_t& row0, uint32_t& rows, uint32_t& tm, uint32_t& tn) {
+__device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t total_rows, uint32_t t, uint32_t tilesN,
+                                             uint32_t& e_out, uint32_t& row0, uint32_t& rows, uint32_t& tm,
+                                             uint32_t& tn) {
   uint32_t first = 0;
   for (int32_t e = 0; e < gp.E; ++e) {
-    const uint32_t lo = (uint32_t)gp.group_off[e], hi = (uint32_t)gp.group_off[e + 1];
+    uint32_t lo, hi;
+    group_rows(gp, e, total_rows, lo, hi);
     const uint32_t cnt = hi - lo;
     const uint32_t mt = (cnt + BM - 1) / BM;
     const uint32_t n = mt * tilesN;
@@ -163,11 +176,12 @@ __device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t t, uint3
   return false;
 }
 
-__device__ __forceinline__ uint32_t grouped_total_tiles(const Groups& gp, uint32_t tilesN) {
+__device__ __forceinline__ uint32_t grouped_total_tiles(const Groups& gp, uint32_t total_rows, uint32_t tilesN) {
   uint32_t total = 0;
   for (int32_t e = 0; e < gp.E; ++e) {
-    const uint32_t cnt = (uint32_t)(gp.group_off[e + 1] - gp.group_off[e]);
-    total += ((cnt + BM - 1) / BM) * tilesN;
+    uint32_t lo, hi;
+    group_rows(gp, e, total_rows, lo, hi);
+    total += ((hi - lo + BM - 1) / BM) * tilesN;
   }
   return total;
 }
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   // list, v -> t = (v % 8) * ceil(total / 8) + v / 8.
   uint32_t total, per_xcd = 0;
   if (GROUPED) {
-    total = grouped_total_tiles(gp, tilesN);
+    total = grouped_total_tiles(gp, M, tilesN);
     per_xcd = (total + 7u) / 8u;
   } else {
     total = tilesM * tilesN;
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
     const uint8_t* sBx = sB;
     if (GROUPED) {
       uint32_t cnt, tm, tn;
-      grouped_tile(gp, t, tilesN, expert, row0, cnt, tm, tn);
+      grouped_tile(gp, M, t, tilesN, expert, row0, cnt, tm, tn);
       m0 = tm * BM;
       n0 = tn * BN;
       rowsA = (cnt - m0) < BM ? (cnt - m0) : BM;

@@ -10,7 +10,26 @@
 //
 // Matrix core: v_mfma_scale_f32_32x32x64_f8f6f4 with A as FP8 (cbsz 0) and
 // B as FP4 (blgp 4).  It issues at the FP8 rate (64 cycles, half the FP4
-// rate).  Per lane of a 32-row block (row i = lane % 32, half j = lane / 32)
+// rate).
+// Exactness: the instruction sums each 16-value K group's products in a
+// fixed-point window anchored at the group's largest E4M3 exponent plus its
+// largest E2M1 exponent (zero and subnormal codes counted at the lowest
+// normal exponent) and truncates each product to a multiple of 2^(anchor -
+// 13) (measured on the device).  A product a * b has its lowest bit at
+// 2^(e_a - 3 + e_b' - 1) (E4M3 keeps 3 fraction bits, E2M1 one; e_b' =
+// max(e_b, 0)), so it is exact when (E_A - e_a) + (E_B - e_b') <= 9; with
+// e_b' in 0..2 that holds whenever the A element is within 7 binades of its
+// group's largest.  Each step therefore runs twice: once on the A bytes
+// whose exponent field is >= 8 (|a| >= 2 before the block scale: exponents
+// 1..8) and once on the others (exponents -6..0, subnormals at -6).  Within
+// either part every nonzero element is within 7 binades of the part's
+// largest, so every product is exact and the accumulator receives the exact
+// group sums: C is the FP32-accumulated exact product, within 1e-5 *
+// sum |a * b| of the FP64 reference.  Both parts are plain E4M3 bytes under
+// the block's own scale, so the E8M0 scales still ride in the instruction.
+// The price is two FP8 instructions per step (the exact W4A8 product runs
+// at half the FP8 rate).
+// Per lane of a 32-row block (row i = lane % 32, half j = lane / 32)
 // and 64-value K step:
 //   A (FP8): bytes 0-15 hold K [16j, 16j + 16), bytes 16-31 hold
 //            K [32 + 16j, 32 + 16j + 16);
@@ -49,13 +68,33 @@ constexpr uint32_t W_STAGE_BYTES = A_REGION + B_REGION + 2u * S_REGION;
 constexpr uint32_t W_NSTAGE = 3;
 constexpr uint32_t W_GROUP_M = 4;
 
-// Operands of one 64-value K step of a wave's 64 x 128 sub-tile.
+// Operands of one 64-value K step of a wave's 64 x 128 sub-tile.  a holds
+// the A bytes as read from LDS; after split_w, a keeps the bytes with
+// exponent field >= 8 and alo the others (zeros in the other's places).
 struct OpsW {
-  v8i a[2];
+  v8i a[2], alo[2];
   v4i b[4];
 };
 
-template <int SUB>
+// Split every E4M3 byte of A by bit 6, the top bit of its exponent field:
+// v_perm with selector byte 12 gives 0x00, 13 gives 0xFF, so the mask byte
+// is 0xFF exactly where bit 6 is set.
+__device__ __forceinline__ void split_w(OpsW& o) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t d = (uint32_t)o.a[r][k];
+      const uint32_t sel = ((d >> 6) & 0x01010101u) | 0x0C0C0C0Cu;
+      const uint32_t hi = d & __builtin_amdgcn_perm(0u, 0u, sel);
+      o.a[r][k] = (int)hi;
+      o.alo[r][k] = (int)(d ^ hi);
+    }
+}
+
+// The 8 MFMAs of one step on one part of A (LO: the small-exponent part);
+// op_sel SUB picks the step's scale byte.
+template <int SUB, bool LO>
 __device__ __forceinline__ void mma_w(v16f (&acc)[2][4], const OpsW& o, const uint32_t (&sa)[2],
                                       const uint32_t (&sb)[4]) {
 #pragma unroll
@@ -63,18 +102,28 @@ __device__ __forceinline__ void mma_w(v16f (&acc)[2][4], const OpsW& o, const ui
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const v8i b8 = __builtin_shufflevector(o.b[c], o.b[c], 0, 1, 2, 3, -1, -1, -1, -1);
-      acc[r][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[r], b8, acc[r][c], 0, 4, SUB, (int)sa[r], SUB,
-                                                                   (int)sb[c]);
+      acc[r][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(LO ? o.alo[r] : o.a[r], b8, acc[r][c], 0, 4, SUB,
+                                                                   (int)sa[r], SUB, (int)sb[c]);
     }
 }
 
-// One LDS read of the next operands after each MFMA: a step has 8 MFMAs and
-// 8 operand reads (A: 2 x 2, B: 4).
+// One LDS read of the next operands after each of the first part's MFMAs: a
+// step has 8 operand reads (A: 2 x 2, B: 4).
 __device__ __forceinline__ void interleave_w() {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+}
+
+// The split of the next operands (80 VALU instructions) among the second
+// part's 8 MFMAs.
+__device__ __forceinline__ void interleave_split() {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0); // VALU
   }
 }
 
@@ -221,21 +270,28 @@ __global__ __launch_bounds__(512, 1) void gemm_w4a8_kernel(const uint8_t* __rest
     asm volatile("" ::: "memory");
     read_ops(0, 0, o0);
     read_scales(0, 0, sa, sb);
+    split_w(o0);
     uint32_t buf = 0;
     for (uint32_t s = 0; s < NS; ++s) {
       // (kept in a scalar register: the copies take their LDS address from one)
       const uint32_t nbuf = __builtin_amdgcn_readfirstlane(buf == 2u ? 0u : buf + 1u);
       read_ops(buf, 1, o1);
-      mma_w<0>(acc, o0, sa, sb);
+      mma_w<0, false>(acc, o0, sa, sb);
       interleave_w();
+      split_w(o1);
+      mma_w<0, true>(acc, o0, sa, sb);
+      interleave_split();
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       dma(s + 3u, buf);
       read_ops(nbuf, 0, o0);
       read_scales(nbuf, s + 1u, sa_n, sb_n);
-      mma_w<1>(acc, o1, sa, sb);
+      mma_w<1, false>(acc, o1, sa, sb);
       interleave_w();
+      split_w(o0);
+      mma_w<1, true>(acc, o1, sa, sb);
+      interleave_split();
 #pragma unroll
       for (int r = 0; r < 2; ++r) sa[r] = sa_n[r];
 #pragma unroll

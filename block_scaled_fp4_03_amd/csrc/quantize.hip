@@ -56,14 +56,21 @@ __device__ __forceinline__ void load8v(const void* x, size_t idx, float v[8]) {
 // Each workgroup pass covers a span of TPB * NL * 16 bytes: every lane
 // issues NL 16-byte loads (a wave's load reads 1 KB contiguous) before it
 // folds any of them; buffer loads bound the last, partial span without a
-// branch.  The max runs on the magnitude bits (for finite values the integer
-// order is the order of |x|).  A dword holds one FP32 value or two BF16
-// values (each the high half of an FP32 value).
+// branch.  The max runs on the magnitude bits (for finite values and
+// infinities the integer order is the order of |x|; NaNs are skipped).  A
+// dword holds one FP32 value or two BF16 values (each the high half of an
+// FP32 value).
 //
 // The grid is small (at most 128 workgroups): the completion protocol below
 // costs two device-scope atomics per workgroup on one address, and those
 // serialise (measured ~9.5 ns each: 2048 workgroups added ~38 us to an
 // otherwise 20 us pass over 134 MB).
+// NaN policy of every tensor maximum (this kernel, the one-launch small
+// path, the fused decode kernels): a NaN element is skipped, as fmaxf skips
+// it.  In magnitude bits a NaN is above +inf (0x7F800000), so it is taken as
+// 0 here.
+__device__ __forceinline__ uint32_t mag_bits_no_nan(uint32_t a) { return a <= 0x7F800000u ? a : 0u; }
+
 template <int DT, int TPB, int NL>
 __global__ __launch_bounds__(TPB) void tensor_amax_kernel(const void* __restrict__ x, size_t nbytes,
                                                           uint32_t* __restrict__ ws, float* __restrict__ ts) {
@@ -83,10 +90,10 @@ __global__ __launch_bounds__(TPB) void tensor_amax_kernel(const void* __restrict
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (DT == kDtF32) {
-          mb = max(mb, w[u][k] & 0x7FFFFFFFu);
+          mb = max(mb, mag_bits_no_nan(w[u][k] & 0x7FFFFFFFu));
         } else {
-          mb = max(mb, (w[u][k] << 16) & 0x7FFF0000u);
-          mb = max(mb, w[u][k] & 0x7FFF0000u);
+          mb = max(mb, mag_bits_no_nan((w[u][k] << 16) & 0x7FFF0000u));
+          mb = max(mb, mag_bits_no_nan(w[u][k] & 0x7FFF0000u));
         }
       }
   }
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const void* __restrict
                                                           uint8_t* __restrict__ scales, uint32_t rows, uint32_t K,
                                                           uint32_t KT, uint32_t KT2, uint32_t total_waves,
                                                           uint64_t seed) {
-  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t wave = blockIdx.x * 4u + (threadIdx.x >> 6);  // < 2^26: the host bounds the grid
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t w0 = wave * (uint32_t)IT;
   if (w0 >= total_waves) return;
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
                                                           const float* __restrict__ tensor_scale, uint32_t rows,
                                                           uint32_t K, uint32_t KT, uint32_t KT2,
                                                           uint32_t total_waves, uint64_t seed) {
-  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t wave = blockIdx.x * 4u + (threadIdx.x >> 6);  // < 2^26: the host bounds the grid
   const uint32_t w0 = wave * (uint32_t)IT;
   if (w0 >= total_waves) return;
   const uint32_t lane = threadIdx.x & 63u;

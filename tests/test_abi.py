@@ -265,3 +265,80 @@ def test_gemm_scale_ranges_are_checked(L):
                            None) == -2
     assert fp4.fp4_gemm_grouped(FAKE, FAKE, big, FAKE, FAKE, 4, FAKE, FAKE, None, None, FAKE, 64, 64, 8192, 0, 1,
                                 None, 0, None) == -2
+
+
+def test_quantize_and_dequantize_grid_limits(L):
+    """The element-wise kernels index their waves and threads in 32 bits and
+    a launch counts its work-items in 32 bits: shapes past that are refused on
+    the host (one 64-lane wave per 32-row-padded row and 512-value slice for
+    the quantisers, one thread per 8 values for dequantisation)."""
+    q, d = fp4.fp4_quantize, fp4.fp4_dequantize
+    # 2^26 waves = 2^32 work-items: refused; one slice fewer fits.
+    assert q(FAKE, 0, FAKE, FAKE, None, 1 << 20, 1 << 15, 0, 0, None, 0, None) == -2   # 2^20 rows x 64 slices
+    assert q(FAKE, 0, FAKE, FAKE, None, 32, 1 << 30, 0, 0, None, 0, None) == -2        # padding rows count too
+    # Shapes inside the limit pass the size check and stop at the next one
+    # (a NULL output), so nothing is launched on these fake pointers.
+    assert q(FAKE, 0, None, FAKE, None, 1, (1 << 29), 0, 0, None, 0, None) == -1       # 32 x 2^20 x 64 < 2^32
+    assert q(FAKE, 0, None, FAKE, None, 1 << 20, (1 << 15) - 512, 0, 0, None, 0, None) == -1
+    assert d(FAKE, FAKE, None, 0, FAKE, 0, 1 << 20, 1 << 15, None) == -2              # 2^32 threads
+    assert d(FAKE, FAKE, None, 0, None, 0, 1 << 19, 1 << 15, None) == -1
+
+
+def test_wrappers_reject_bad_tensors_before_the_library():
+    """The Python wrappers refuse, before any library call, tensors the C ABI
+    would misread: int64 indices (read as int32 halves), non-contiguous views
+    (silently wrong layout), host tensors (a host pointer handed to a kernel),
+    wrong shapes and short buffers."""
+    import torch
+    need = fp4._need
+    ok = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        need(torch.zeros(8, dtype=torch.int64), "row_idx", (torch.int32,))
+    with pytest.raises(ValueError, match="contiguous"):
+        need(torch.zeros((8, 8), dtype=torch.float32).t(), "x", (torch.float32,))
+    with pytest.raises(ValueError, match="contiguous"):
+        need(torch.zeros((8, 16), dtype=torch.float32)[:, :8], "x", (torch.float32,))
+    with pytest.raises(ValueError, match="dimensions"):
+        need(torch.zeros((2, 4), dtype=torch.int32), "row_idx", (torch.int32,), ndim=1)
+    with pytest.raises(ValueError, match="elements"):
+        need(ok, "group_off", (torch.int32,), 9)
+    with pytest.raises(ValueError, match="GPU"):
+        need(ok, "group_off", (torch.int32,), 8)
+    with pytest.raises(TypeError):
+        need(np_array := [1, 2], "x")  # noqa: F841
+    # Whole calls with host tensors stop in the wrapper, not in a kernel.
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.quantize(x, fp4.MXFP4)
+    with pytest.raises(TypeError):
+        fp4.quantize(x.to(torch.float64), fp4.MXFP4)
+    with pytest.raises(ValueError, match="contiguous"):
+        fp4.quantize(torch.zeros((64, 4), dtype=torch.float32).t(), fp4.MXFP4)
+    with pytest.raises(ValueError, match="dimensions"):
+        fp4.quantize(torch.zeros(64, dtype=torch.float32), fp4.MXFP4)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.hadamard16(x, seed=1)
+    q = fp4.Quantized(torch.zeros((4, 32), dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8), None,
+                      fp4.MXFP4, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.gemm(q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.dequantize(q)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.gemm_ex(q, q)
+    short = fp4.Quantized(torch.zeros((4, 16), dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8), None,
+                          fp4.MXFP4, 4, 64)
+    with pytest.raises(ValueError, match="elements"):
+        fp4.gemm(short, q)
+    nv = fp4.Quantized(torch.zeros((4, 32), dtype=torch.uint8), torch.zeros(512, dtype=torch.uint8), None,
+                       fp4.NVFP4, 4, 64)
+    with pytest.raises(ValueError, match="tensor scale"):
+        fp4.gemm(nv, nv)
+    with pytest.raises(TypeError):
+        fp4.gemm("a", q)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.gemm_grouped(q, ok, ok, torch.zeros(64, dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8),
+                         16, 64, fp4.MXFP4)
+    with pytest.raises(ValueError, match="GPU"):
+        fp4.gemm_nvfp4_act(x, nv)
+

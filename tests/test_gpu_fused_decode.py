@@ -105,6 +105,9 @@ def test_fused_decode_8192_sampled(orc, M):
     rx = orc.quantize(x, orc.FMT_NVFP4)
     assert to_host(ts)[0] == np.float32(rx[3])
     cols = np.random.default_rng(M).choice(8192, 64, replace=False)
-    rw = orc.quantize(w[cols], orc.FMT_NVFP4, tensor_scale=float(to_host(qw.tensor_scale)[0]))
+    # The oracle's own tensor scale of the whole weight (never the GPU's).
+    ts_w = orc.nvfp4_tensor_scale(orc.tensor_amax(w))
+    assert to_host(qw.tensor_scale)[0] == np.float32(ts_w)
+    rw = orc.quantize(w[cols], orc.FMT_NVFP4, tensor_scale=ts_w)
     Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], M, 64, 8192, orc.FMT_NVFP4, tsA=rx[3], tsB=rw[3])
     assert_gemm_close(orc, to_host(C)[:, cols], Cref, T, True, "fused decode 8192 M=%d" % M)

@@ -195,50 +195,68 @@ def test_exact_small_exponent_range_bit_exact(orc):
     np.testing.assert_array_equal(C.astype(np.float64), Cref)
 
 
-def test_mxfp4_8192_sampled(orc):
-    """The 8192^3 MXFP4 workload in the benchmark's launch configuration; 24
-    sampled rows x 24 sampled columns against the oracle (which quantises just
-    those rows of A and B itself)."""
+def _band_picks(n, band, seed):
+    """One index in each `band`-wide band of range(n) (the first band's is 0,
+    the last band's n - 1): with band = 256, one row (or column) in every
+    output tile row (or column)."""
+    g = np.random.default_rng(seed)
+    starts = np.arange(0, n, band)
+    picks = starts + g.integers(0, band, starts.size)
+    picks = np.minimum(picks, n - 1)
+    picks[0], picks[-1] = 0, n - 1
+    return picks
+
+
+def test_mxfp4_8192_every_tile(orc):
+    """The 8192^3 MXFP4 workload in the benchmark's launch configuration,
+    every 256 x 256 output tile checked: one row in each 256-row band against
+    all 8192 columns, and one column in each 256-column band against all 8192
+    rows, each against the oracle (which quantises the operands itself)."""
     import block_scaled_fp4_03_amd as fp4
     import torch
+    n = 8192
     a, b = synth.mxfp4_8192()
     say("gemm mxfp4_8192 full size")
     qa = fp4.quantize(to_dev(a), 0)
     qb = fp4.quantize(to_dev(b), 0)
-    C = fp4.gemm(qa, qb, out_dtype=torch.bfloat16)
-    g = np.random.default_rng(3)
-    rows = np.sort(np.concatenate([[0, 8191], g.choice(8192, 22, replace=False)]))
-    cols = np.sort(np.concatenate([[0, 8191], g.choice(8192, 22, replace=False)]))
-    Cs = to_host(C)[np.ix_(rows, cols)]
-    ra = orc.quantize(a[rows], 0)
-    rb = orc.quantize(b[cols], 0)
-    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 8192, 0)
-    assert_gemm_close(orc, Cs, Cref, T, True, "mxfp4_8192 sampled")
+    C = to_host(fp4.gemm(qa, qb, out_dtype=torch.bfloat16))
+    rows, cols = _band_picks(n, 256, 3), _band_picks(n, 256, 33)
+    ra, rb_all = orc.quantize(a[rows], 0), orc.quantize(b, 0)
+    Cref, T = orc.gemm(ra[0], ra[1], rb_all[0], rb_all[1], rows.size, n, n, 0)
+    assert_gemm_close(orc, C[rows], Cref, T, True, "mxfp4_8192 one row per 256-row band")
+    del rb_all
+    ra_all, rb = orc.quantize(a, 0), orc.quantize(b[cols], 0)
+    Cref, T = orc.gemm(ra_all[0], ra_all[1], rb[0], rb[1], n, cols.size, n, 0)
+    assert_gemm_close(orc, C[:, cols], Cref, T, True, "mxfp4_8192 one column per 256-column band")
 
 
-def test_nvfp4_mlp_sampled(orc):
+def test_nvfp4_mlp_every_tile(orc):
     """The 4096 x 14336 x 4096 NVFP4 workload (BF16 activations quantised on
-    the fly, weights pre-quantised) in the benchmark's launch configuration;
-    24 x 24 sampled outputs against the oracle, which quantises those rows
-    itself with the tensor scales it computes from the whole operands."""
+    the fly, weights pre-quantised) in the benchmark's launch configuration,
+    every output tile checked: one row per 256-row band x all columns, one
+    column per 256-column band x all rows, against the oracle, which
+    quantises with the tensor scales it computes from the whole operands."""
     import block_scaled_fp4_03_amd as fp4
     import torch
+    M, N, K = 4096, 14336, 4096
     a, w = synth.nvfp4_mlp()
     say("gemm nvfp4_mlp full size")
     qa = fp4.quantize(to_dev(a), 1)
     qw = fp4.quantize(to_dev(w), 1)
-    C = fp4.gemm(qa, qw, out_dtype=torch.bfloat16)
-    g = np.random.default_rng(4)
-    rows = np.sort(np.concatenate([[0, 4095], g.choice(4096, 22, replace=False)]))
-    cols = np.sort(np.concatenate([[0, 14335], g.choice(14336, 22, replace=False)]))
-    Cs = to_host(C)[np.ix_(rows, cols)]
+    C = to_host(fp4.gemm(qa, qw, out_dtype=torch.bfloat16))
     ts_a = orc.nvfp4_tensor_scale(orc.tensor_amax(a))
     ts_w = orc.nvfp4_tensor_scale(orc.tensor_amax(w))
     assert to_host(qa.tensor_scale)[0] == np.float32(ts_a) and to_host(qw.tensor_scale)[0] == np.float32(ts_w)
+    rows, cols = _band_picks(M, 256, 4), _band_picks(N, 256, 44)
     ra = orc.quantize(a[rows], 1, tensor_scale=ts_a)
-    rb = orc.quantize(w[cols], 1, tensor_scale=ts_w)
-    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], rows.size, cols.size, 4096, 1, tsA=ts_a, tsB=ts_w)
-    assert_gemm_close(orc, Cs, Cref, T, True, "nvfp4_mlp sampled")
+    rw = orc.quantize(w, 1, tensor_scale=ts_w)
+    Cref, T = orc.gemm(ra[0], ra[1], rw[0], rw[1], rows.size, N, K, 1, tsA=ts_a, tsB=ts_w)
+    assert_gemm_close(orc, C[rows], Cref, T, True, "nvfp4_mlp one row per 256-row band")
+    del rw
+    ra = orc.quantize(a, 1, tensor_scale=ts_a)
+    rw = orc.quantize(w[cols], 1, tensor_scale=ts_w)
+    Cref, T = orc.gemm(ra[0], ra[1], rw[0], rw[1], M, cols.size, K, 1, tsA=ts_a, tsB=ts_w)
+    assert_gemm_close(orc, C[:, cols], Cref, T, True, "nvfp4_mlp one column per 256-column band")
 
 
 # M <= 8 within its K reach takes the block-sum decode kernel; otherwise the
@@ -394,10 +412,12 @@ def test_grouped_gemm(orc, counts, N, K, bf16_out):
     assert_gemm_close(orc, Cg.reshape(-1), Cref, T, bf16_out, "grouped")
 
 
-def test_grouped_moe_full_size_sampled(orc):
+def test_grouped_moe_full_size(orc):
     """The MoE workload: 32 experts (5760 x 2880 MXFP4 weights N(0, 0.02^2)),
-    16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4; sampled
-    output rows from every non-empty expert x 24 columns against the oracle."""
+    16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4.  Every
+    row of each expert with at most 256 rows, a whole 256-row band of each
+    larger expert (at a random offset), against one column in each 256-column
+    band, checked against the oracle."""
     import block_scaled_fp4_03_amd as fp4
     import torch
     E, N, K, T_rows = 32, 5760, 2880, 16384
@@ -417,17 +437,84 @@ def test_grouped_moe_full_size_sampled(orc):
                          out_dtype=torch.bfloat16)
     Ch = to_host(C)
     g = np.random.default_rng(5)
-    cols = np.sort(np.concatenate([[0, N - 1], g.choice(N, 22, replace=False)]))
+    cols = _band_picks(N, 256, 55)
     checked = 0
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
             continue
-        rs = np.unique(np.concatenate([[lo, hi - 1], g.integers(lo, hi, 2)]))
+        if hi - lo <= 256:
+            rs = np.arange(lo, hi)
+        else:
+            start = lo + int(g.integers(0, hi - lo - 256 + 1))
+            rs = np.arange(start, start + 256)
         w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
         rw = orc.quantize(w[cols], 0)
         rx = orc.quantize(x[row_idx[rs]], 0)
         Cref, T = orc.gemm(rx[0], rx[1], rw[0], rw[1], rs.size, cols.size, K, 0)
         assert_gemm_close(orc, Ch[np.ix_(rs, cols)], Cref, T, True, "moe expert %d" % e)
         checked += rs.size
-    assert checked > 50
+    assert checked > 2000
+
+
+@pytest.mark.parametrize("offsets", [[0, 60, 40, 130], [0, -10, 50, 100], [0, 30, 30, 2 ** 31 - 1]])
+def test_grouped_malformed_offsets_stay_in_bounds(orc, offsets):
+    """group_off that decreases, goes negative or runs past total_rows: the
+    kernel clamps every group to [0, total_rows], so nothing past C's
+    total_rows rows is written.  C and row_idx are allocated with guard rows
+    beyond what the call is told, so a wrong clamp would show as a changed
+    guard, not as an access outside the allocation.  Rows that only a
+    well-formed, clamped group covers equal the oracle's."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    E, total, N, K, T_rows, guard = 3, 100, 64, 64, 64, 300
+    x = synth.gaussian(501, (T_rows, K))
+    ws = [synth.gaussian(510 + e, (N, K), std=0.05) for e in range(E)]
+    qa, ra = _quant_both(orc, x, 0)
+    codes, scales, refs = _quant_experts(orc, ws, 0)
+    ri = np.random.default_rng(7).integers(0, T_rows, total + guard).astype(np.int32)
+    off = np.array(offsets, np.int64).astype(np.int32)
+    ri_d, off_d = to_dev(ri), to_dev(off)
+    C = torch.full((total + guard, N), 1234.5, dtype=torch.float32, device="cuda")
+    say("grouped malformed offsets %s" % offsets)
+    rc = fp4.fp4_gemm_grouped(qa.codes.data_ptr(), qa.scales.data_ptr(), T_rows, ri_d.data_ptr(), off_d.data_ptr(),
+                              E, codes.data_ptr(), scales.data_ptr(), None, None, C.data_ptr(), total, N, K, 0,
+                              fp4.F32, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    Ch = to_host(C)
+    assert (Ch[total:] == np.float32(1234.5)).all(), "rows past total_rows were written"
+    # the clamped groups: [lo, hi) with 0 <= lo <= hi <= total
+    cl = [min(max(int(v), 0), total) for v in offsets]
+    spans = []
+    for e in range(E):
+        lo, hi = cl[e], max(cl[e + 1], cl[e])
+        spans.append((lo, hi))
+    for e, (lo, hi) in enumerate(spans):
+        rows = [r for r in range(lo, hi) if all(not (l2 <= r < h2) for j, (l2, h2) in enumerate(spans) if j != e)]
+        if not rows:
+            continue
+        rows = np.array(rows)
+        rx = orc.quantize(x[ri[rows]], 0)
+        Cref, T = orc.gemm(rx[0], rx[1], refs[e][0], refs[e][1], rows.size, N, K, 0)
+        assert_gemm_close(orc, Ch[rows], Cref, T, False, "malformed offsets expert %d" % e)
+
+
+def test_wrapper_rejects_int64_group_offsets():
+    """int64 indices (torch's default from cumsum / argsort) are refused before
+    the library is called: read as int32 halves they would make group sizes
+    wrap."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    x = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    qa = fp4.quantize(x, 0)
+    codes = torch.zeros((2, 64, 32), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((2, fp4.fp4_scale_bytes(0, 64, 64)), dtype=torch.uint8, device="cuda")
+    ri = torch.arange(10, device="cuda")                       # int64
+    off = torch.tensor([0, 4, 10], device="cuda")              # int64
+    with pytest.raises(TypeError):
+        fp4.gemm_grouped(qa, ri, off.int(), codes, scales, 64, 64, 0)
+    with pytest.raises(TypeError):
+        fp4.gemm_grouped(qa, ri.int(), off, codes, scales, 64, 64, 0)
+    with pytest.raises(ValueError, match="contiguous"):
+        fp4.gemm_grouped(qa, torch.arange(20, device="cuda", dtype=torch.int32)[::2], off.int(), codes, scales,
+                         64, 64, 0)

@@ -127,3 +127,102 @@ def test_large_bf16_multi_item_path(orc, fmt):
     and a ragged last slice), with edge values; bit-exact, all formats."""
     x = synth.to_bf16_bits(_special(4100, 4000, 97 + fmt))
     _run(orc, fmt, x)
+
+
+# ---- dense sweeps of the hardware rounding paths ------------------------------
+# Every E2M1 code the quantisers write comes from the matrix core's FP32 ->
+# FP4 converter, and every NVFP4 quotient |x| / d from a correctly rounded
+# reciprocal with two corrections: the sweeps below put inputs on and next to
+# every decision point of both.
+MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+
+
+def _around(v):
+    """v and its float32 neighbours one ulp below and above."""
+    v = np.asarray(v, np.float32)
+    return np.concatenate([np.nextafter(v, np.float32(-np.inf)), v, np.nextafter(v, np.float32(np.inf))])
+
+
+def _e2m1_sweep_matrix():
+    """One 32-block per (binade e, sign): element 0 is +-6 * 2^e (so the block
+    exponent is e under both MXFP4 rules), the other 31 hold every E2M1
+    midpoint t * 2^e and its two float32 neighbours (21 values), the grid
+    points 0.5, 1, 1.5, 2, 3, 4, 6 and 6 one ulp below, and -0 / 0, with signs
+    alternating.  e runs over every binade whose block maximum is a finite
+    FP32 value, 2^-127 .. 2^125 (midpoints reach FP32 subnormals)."""
+    rows = []
+    for e in range(-127, 126):
+        for sign in (1.0, -1.0):
+            p = np.float32(2.0) ** np.float32(e) if e > -127 else np.float32(np.ldexp(1.0, -127))
+            mids = _around(MIDPOINTS * p)                             # 21
+            grid = np.array([0.5, 1.0, 2.0, 4.0], np.float32) * p      # 4
+            extra = np.concatenate([grid, [np.nextafter(np.float32(6.0) * p, np.float32(0))],
+                                    [np.float32(0.0), np.float32(-0.0)], grid[:2] * np.float32(3.0),
+                                    [np.float32(6.0) * p]])
+            blk = np.concatenate([[np.float32(6.0) * p], mids, extra]).astype(np.float32)
+            assert blk.size == 32
+            sgn = np.where(np.arange(32) % 2 == 0, sign, -sign).astype(np.float32)
+            sgn[0] = sign
+            rows.append(blk * sgn)
+    blocks = np.stack(rows)                      # (506, 32)
+    return blocks.reshape(-1, 32 * 22)           # 23 rows of 22 blocks
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_e2m1_converter_sweep_every_binade(orc, fmt):
+    x = _e2m1_sweep_matrix()
+    assert np.isfinite(x).all()
+    _run(orc, fmt, x)
+
+
+def _nvfp4_division_sweep(s_t):
+    """For every finite nonzero E4M3 byte sb (1..126): two 16-blocks whose
+    maximum is 6 * d, d = e4m3(sb) * s_t (FP32), so the block scale is sb; the
+    other 30 elements put |x| / d on and one ulp next to each E2M1 decision
+    point (0.25, 0.75, ..., 5), both signs."""
+    import oracle
+    blocks = []
+    for sb in range(1, 127):
+        d = np.float32(np.float32(oracle.e4m3_value(sb)) * np.float32(s_t))
+        amax = np.float32(np.float32(6.0) * d)
+        probes = _around(MIDPOINTS * d)                               # 21
+        probes = np.concatenate([probes, -probes[:9]])                # 30
+        for h in range(2):
+            blk = np.concatenate([[amax if h == 0 else -amax], probes[15 * h:15 * h + 15]]).astype(np.float32)
+            blocks.append(blk)
+    return np.concatenate(blocks).reshape(9, -1)                      # 9 rows of 28 blocks
+
+
+@pytest.mark.parametrize("s_t", [1.0, 2.0 ** -10, 0.0123, 3.7e-5, 1.3e-30, 5.5e3])
+def test_nvfp4_division_sweep_every_scale_byte(orc, s_t):
+    x = _nvfp4_division_sweep(s_t)
+    assert np.isfinite(x).all()
+    q, ref = _run(orc, 1, x, ts=float(np.float32(s_t)))
+    # every E4M3 byte 1..126 occurs as a block scale
+    canon = orc.quantize(x, 1, tensor_scale=float(np.float32(s_t)))[2]
+    assert set(range(1, 127)) <= set(np.unique(canon).tolist())
+
+
+@pytest.mark.parametrize("rows,K", [(16, 4096), (512, 4096)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_nvfp4_nan_skipped_by_tensor_maximum(orc, rows, K, bf16):
+    """One NaN in the tensor: every path's tensor maximum skips it, as the
+    oracle's does, below the one-launch threshold (256 KB: 16 x 4096) and
+    above it (512 x 4096: amax kernel, then quantise).  s_t and every scale
+    byte equal the oracle's; codes equal everywhere except at the NaN
+    itself (a NaN input has no defined code)."""
+    x = synth.gaussian(77 + rows, (rows, K))
+    r, k = rows // 2, 123
+    x[r, k] = np.float32(np.nan)
+    if bf16:
+        x = synth.to_bf16_bits(x)
+    import block_scaled_fp4_03_amd as fp4
+    say("nvfp4 NaN rows=%d K=%d bf16=%s" % (rows, K, bf16))
+    q = fp4.quantize(to_dev(x), fp4.NVFP4)
+    codes, scales, _, ts = orc.quantize(x, 1)
+    assert np.isfinite(ts)
+    assert to_host(q.tensor_scale)[0] == np.float32(ts)
+    np.testing.assert_array_equal(to_host(q.scales), scales)
+    got = to_host(q.codes).copy()
+    got[r, k // 2] = codes[r, k // 2] = 0
+    np.testing.assert_array_equal(got, codes)
