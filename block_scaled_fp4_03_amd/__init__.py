@@ -25,7 +25,8 @@ Q_SR, Q_2D = 2, 4
 OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP = 0, 1, 2, 3
 ACT_NONE, ACT_RELU = 0, 1
 
-FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_sr", "fp4_quantize_ex",
+FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_noalloc", "fp4_quantize_sr",
+             "fp4_quantize_ex",
              "fp4_hadamard16", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
              "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_gemm_w4a8",
              "fp4_status_string")
@@ -52,6 +53,7 @@ def lib():
             "fp4_scale_bytes": (I64, [I32, I64, I64]),
             "fp4_workspace_size": (SZ, [I32, I32, I64, I64, I64, I32]),
             "fp4_quantize": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P, SZ, P]),
+            "fp4_quantize_noalloc": (I32, [P, I32, P, P, P, I64, I64, I32, U32, P]),
             "fp4_quantize_sr": (I32, [P, I32, P, P, P, I64, I64, I32, U32, ctypes.c_uint64, P, SZ, P]),
             "fp4_quantize_ex": (I32, [P, I32, P, P, P, I64, I64, I32, U32, ctypes.c_uint64, P, SZ, P]),
             "fp4_hadamard16": (I32, [P, I32, P, I32, I64, I64, ctypes.c_uint64, P]),
@@ -89,6 +91,10 @@ def fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, f
                  stream):
     return lib().fp4_quantize(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, workspace,
                               workspace_bytes, stream)
+
+
+def fp4_quantize_noalloc(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, stream):
+    return lib().fp4_quantize_noalloc(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, stream)
 
 
 def fp4_quantize_sr(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, seed, workspace,

@@ -113,6 +113,34 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
                        workspace_bytes, 0ull, stream);
 }
 
+int fp4_quantize_noalloc(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                         int64_t rows, int64_t K, int in_dtype, unsigned flags, void* stream) {
+  if (flags & ~FP4_TS_GIVEN) return FP4_ERR_FLAGS;
+  // The same host-side validation as fp4_quantize, before any HIP call.
+  if (!qfmt_ok(fmt)) return FP4_ERR_FMT;
+  if (!dtype_ok(in_dtype)) return FP4_ERR_DTYPE;
+  if (rows < 0 || K < 0 || rows > kMaxDim || K > kMaxDim || K % block_of(fmt) != 0) return FP4_ERR_SHAPE;
+  if (!quantize_grid_fits(rows, K)) return FP4_ERR_SHAPE;
+  if (rows == 0 || K == 0) return FP4_OK;
+  const size_t need = fp4_workspace_size(FP4_OP_QUANTIZE, fmt, rows, 0, K, 0);
+  if (need > fp4::kScratchBytes) return FP4_ERR_WORKSPACE;
+  // NVFP4 computing its own tensor scale takes the scratch as its workspace
+  // (inputs up to 256 KB reduce the maximum in one launch and leave it
+  // untouched).
+  const bool uses_ws = fmt == FP4_NVFP4 && !(flags & FP4_TS_GIVEN);
+  if (!uses_ws)
+    return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, nullptr, 0, 0ull,
+                         stream);
+  // Argument errors first, so that a refused call makes no HIP call at all.
+  if (!x || !codes || !block_scales || !tensor_scale) return FP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(block_scales, 4) || !aligned(tensor_scale, 4))
+    return FP4_ERR_ALIGN;
+  void* ws = nullptr;
+  if (fp4::scratch_for_current_device(as_stream(stream), &ws) != hipSuccess) return FP4_ERR_HIP;
+  return quantize_impl(x, fmt, codes, block_scales, tensor_scale, rows, K, in_dtype, flags, ws, fp4::kScratchBytes,
+                       0ull, stream);
+}
+
 int fp4_quantize_sr(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                     int64_t rows, int64_t K, int in_dtype, unsigned flags, uint64_t seed, void* workspace,
                     size_t workspace_bytes, void* stream) {

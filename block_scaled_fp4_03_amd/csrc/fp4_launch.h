@@ -8,6 +8,14 @@
 
 namespace fp4 {
 
+// Scratch held by the library for fp4_quantize_noalloc (quantize.hip): the
+// current device's copy of a static device array of kScratchBytes, found
+// with hipGetSymbolAddress on the first call per device (which also clears
+// it on `stream`).  At most kMaxDevices devices.
+constexpr uint32_t kScratchBytes = 256;
+constexpr uint32_t kMaxDevices = 64;
+hipError_t scratch_for_current_device(hipStream_t stream, void** ptr);
+
 // Quantisation (quantize.hip).
 hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* ws, float* tensor_scale,
                               hipStream_t stream);

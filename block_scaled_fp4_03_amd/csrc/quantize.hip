@@ -19,7 +19,56 @@
 
 #include <float.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace fp4 {
+
+// ---------------------------------------------------------------------------
+// Library-held scratch for fp4_quantize_noalloc (callers that cannot
+// allocate: code under graph capture, serving loops, allocation-free
+// harnesses).  Each GPU the library runs on holds one copy of this array
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in): it takes the device address
+// from hipGetSymbolAddress once per device, with that device current, and
+// passes that.  Every call on one GPU shares its copy, so overlapping calls
+// on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4u];
+
+namespace {
+__global__ void clear_words_kernel(uint32_t* __restrict__ w, uint32_t n) {
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+}  // namespace
+
+hipError_t scratch_for_current_device(hipStream_t stream, void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex init;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= (int)kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(init);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      // The control words must start at zero; every completed call leaves
+      // them zero again.  A kernel, not a memset, so that a first call made
+      // under graph capture records a plain kernel node.
+      clear_words_kernel<<<1, 64, 0, stream>>>(static_cast<uint32_t*>(p), kScratchBytes / 4u);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 namespace {
 

@@ -24,7 +24,9 @@
  *     null stream).  Every call is asynchronous on `stream`: it enqueues work
  *     and returns; nothing is copied to or from the host, no call synchronises.
  *   - The caller owns and allocates every buffer, workspace included.  The
- *     library never allocates or frees memory and keeps no global mutable state.
+ *     library never allocates or frees memory and keeps no global mutable
+ *     state, with one exception: fp4_quantize_noalloc's scratch array, a
+ *     static device array of 256 bytes on each GPU the library runs on.
  *   - Argument errors return a negative fp4_status before any HIP call is made,
  *     so they are reported synchronously and leave the stream untouched.  A
  *     failed kernel launch returns FP4_ERR_HIP.  Faults inside a kernel surface
@@ -154,6 +156,30 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
 int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/* fp4_quantize for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, rules, errors and bits as fp4_quantize (flags:
+ * FP4_TS_GIVEN only), without the workspace: where fp4_quantize would use one
+ * (NVFP4 computing its own tensor scale over more than 256 KB of input), the
+ * running maximum and completion counter live in a scratch array the library
+ * holds, a static device array of 256 bytes on each GPU (held until the
+ * process ends).  The call allocates nothing and calls no allocating
+ * routine.
+ *   The first call on a device looks the array up for that device (which must
+ *   be current) and enqueues a one-workgroup kernel on `stream` that clears
+ *   it; every later call leaves its control words zero when its work
+ *   completes.
+ *   All calls on one GPU share that GPU's array: calls that may run at the
+ *   same time on one GPU (different streams, no ordering between them) race
+ *   and give wrong tensor scales.  Order them, or use fp4_quantize with a
+ *   workspace per stream.
+ * Errors: as fp4_quantize; FP4_ERR_WORKSPACE if the operation needed more
+ * than the array's 256 bytes (no format needs more than 8 today);
+ * FP4_ERR_HIP if the array cannot be located on the current device or the
+ * clearing kernel fails to launch. */
+int fp4_quantize_noalloc(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
+                         int64_t rows, int64_t K, int in_dtype, unsigned flags, void* stream);
 
 /* fp4_quantize with stochastic rounding of the elements (NVFP4 video
  * transcript, the training recipe's fourth part: a value between two

@@ -342,3 +342,21 @@ def test_wrappers_reject_bad_tensors_before_the_library():
     with pytest.raises(ValueError, match="GPU"):
         fp4.gemm_nvfp4_act(x, nv)
 
+
+def test_quantize_noalloc_argument_errors(L):
+    """fp4_quantize_noalloc validates like fp4_quantize, before any HIP call
+    (the scratch lookup included)."""
+    q = fp4.fp4_quantize_noalloc
+    assert q(FAKE, 9, FAKE, FAKE, FAKE, 4, 64, 0, 0, None) == -4
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, 4, 64, 3, 0, None) == -5
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, fp4.Q_SR, None) == -8      # only FP4_TS_GIVEN
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 40, 0, 0, None) == -2
+    assert q(FAKE, 0, FAKE, FAKE, None, 1 << 20, 1 << 15, 0, 0, None) == -2
+    assert q(None, 1, None, None, None, 0, 64, 0, 0, None) == 0
+    # NVFP4 above 256 KB: argument errors come before the scratch lookup.
+    assert q(FAKE, 1, FAKE, FAKE, None, 1024, 1024, 0, 0, None) == -1
+    assert q(None, 1, FAKE, FAKE, FAKE, 1024, 1024, 0, 0, None) == -1
+    assert q(ODD, 1, FAKE, FAKE, FAKE, 1024, 1024, 0, 0, None) == -3
+    # Paths without scratch validate as fp4_quantize does.
+    assert q(FAKE, 0, None, FAKE, None, 4, 64, 0, 0, None) == -1
+    assert q(FAKE, 1, FAKE, FAKE, None, 4, 64, 0, 0, None) == -1
