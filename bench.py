@@ -244,16 +244,19 @@ def mxfp4_gemm_8192(torch, fp4, synth, args):
     tflops = gemm_flops(n, n, n) / (ms * 1e-3) / 1e12
     # Clock and power under the same load: 2.5 s of the same steps after the
     # timed ones (the driver's readings need longer than the timed region).
+    if args.telemetry_s <= 0:
+        return dict(ms=ms, tflops=tflops, a=a, b=b, telemetry=None)
     with Telemetry() as tel:
         t0, i = time.perf_counter(), 0
-        while time.perf_counter() - t0 < 2.5:
+        while time.perf_counter() - t0 < args.telemetry_s:
             step(i)
             i += 1
             if i % 32 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
     return dict(ms=ms, tflops=tflops, a=a, b=b,
-                telemetry=tel.summary("2.5 s of headline steps right after the timed ones (first 1 s dropped)"))
+                telemetry=tel.summary("%.1f s of headline steps right after the timed ones (first 1 s dropped)"
+                                      % args.telemetry_s))
 
 
 def mxfp4_gemm_requant_8192(torch, fp4, synth, a, b):
@@ -538,6 +541,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--settle", type=float, default=SETTLE_S,
                    help="seconds of untimed steps before each workload's warm-up (clock ramp)")
+    p.add_argument("--telemetry-s", type=float, default=2.5,
+                   help="seconds of headline steps sampled for clock and power after the timed ones (0: none)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device copy (x*1 -> y) 3 times, to scale the HBM byte counters")
     return p.parse_args()
