@@ -394,6 +394,138 @@ def cpu_baseline_gemm(a, b, K, budget_s=12.0):
                       "8192^3 workload, %.1f s" % (cols, cols, K, dt)}
 
 
+# ---- the oracle on every config (python bench.py --cpu-baseline-all) ---------
+def _host_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_worker(budget_s):
+    """Times the oracle (quantise + FP64 GEMM) on every config with this
+    process's OpenMP thread count; prints one JSON line.  The quantisers run
+    in full; a GEMM that would take longer than `budget_s` runs on a slab of
+    output rows (or weight rows) and is scaled linearly to the full problem
+    (the oracle's cost per output element is the same for every element)."""
+    import oracle
+    import synth
+    oracle.build()
+    oracle.lib()
+
+    def timed(fn, *a, **kw):
+        t0 = time.perf_counter()
+        r = fn(*a, **kw)
+        return r, time.perf_counter() - t0
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+
+    def gemm_slab(ra, rb, rows_a, rows_b, K, fmt, scale_rows_to, **kw):
+        """FP64 GEMM of a slab of A's rows against rb; rows sized so the slab
+        takes about budget_s (the oracle runs its threads over output rows:
+        at least 4 rows per thread, a multiple of the thread count); returns
+        (seconds for scale_rows_to rows, slab rows)."""
+        probe = min(rows_a, threads)
+        _, tp = timed(oracle.gemm, np.ascontiguousarray(ra[0][:probe]), ra[1], rb[0], rb[1], probe, rows_b, K, fmt, **kw)
+        rows = int(max(4 * threads, min(rows_a, probe * budget_s / max(tp, 1e-4))))
+        rows = min(rows_a, (rows + threads - 1) // threads * threads)
+        # a row slab of the quantised A: codes rows are contiguous, and the
+        # scale tiles of the first `rows` rows are the first ceil(rows/32) tiles
+        _, ts = timed(oracle.gemm, np.ascontiguousarray(ra[0][:rows]), ra[1], rb[0], rb[1], rows, rows_b, K, fmt, **kw)
+        return ts * scale_rows_to / rows, rows
+
+    out = {}
+    # 1. MXFP4 256^3, FP32 inputs, full
+    a, b = synth.mxfp4_256()
+    (ra, tqa), (rb, tqb) = timed(oracle.quantize, a, 0), timed(oracle.quantize, b, 0)
+    _, tg = timed(oracle.gemm, ra[0], ra[1], rb[0], rb[1], 256, 256, 256, 0)
+    out["mxfp4_256"] = {"quantize_s": tqa + tqb, "gemm_s": tg, "step_s": tqa + tqb + tg, "slab": "none (full)",
+                        "flop": gemm_flops(256, 256, 256)}
+    # 2. NVFP4 decode: X quantised in full; GEMM over a slab of weight rows
+    #    (all M activation rows), scaled to N = 8192
+    w = synth.nvfp4_decode_weight()
+    rw, tqw = timed(oracle.quantize, w, 1)
+    del w
+    for M in (1, 8, 32):
+        x = synth.nvfp4_decode_act(M)
+        rx, tqx = timed(oracle.quantize, x, 1)
+        # (the oracle's sampled product runs its threads over the outputs, so
+        # a decode shape of 1-32 rows still uses every thread)
+        def outputs(nr):
+            return np.repeat(np.arange(M), nr), np.tile(np.arange(nr), M)
+        r, c = outputs(64)
+        _, t1 = timed(oracle.gemm_sampled, rx[0], rx[1], rw[0], rw[1], M, 8192, 8192, 1, r, c, tsA=rx[3], tsB=rw[3])
+        nrows = int(max(64, min(8192, 64 * budget_s / max(t1, 1e-4)))) // 64 * 64
+        r, c = outputs(nrows)
+        _, ts = timed(oracle.gemm_sampled, rx[0], rx[1], rw[0], rw[1], M, 8192, 8192, 1, r, c, tsA=rx[3], tsB=rw[3])
+        tg = ts * 8192 / nrows
+        out["nvfp4_decode_m%d" % M] = {"quantize_s": tqx, "gemm_s": tg, "step_s": tqx + tg,
+                                       "slab": "%d of 8192 weight rows" % nrows if nrows < 8192 else "none (full)",
+                                       "weight_quantize_offline_s": tqw, "flop": gemm_flops(M, 8192, 8192)}
+    del rw
+    # 3. MXFP4 8192^3: both operands quantised in full; GEMM on a slab of A rows
+    a, b = synth.mxfp4_8192()
+    (ra, tqa), (rb, tqb) = timed(oracle.quantize, a, 0), timed(oracle.quantize, b, 0)
+    del a, b
+    tg, rows = gemm_slab(ra, rb, 8192, 8192, 8192, 0, 8192)
+    out["mxfp4_8192"] = {"quantize_s": tqa + tqb, "gemm_s": tg, "step_s": tg,
+                         "slab": "%d of 8192 rows of A" % rows, "flop": gemm_flops(8192, 8192, 8192),
+                         "note": "the benchmark's step takes pre-quantised operands; quantize_s is reported apart"}
+    del ra, rb
+    # 4. NVFP4 MLP: A (BF16) and W quantised in full; GEMM on a slab of A rows
+    a, w = synth.nvfp4_mlp()
+    (ra, tqa), (rw, tqw) = timed(oracle.quantize, a, 1), timed(oracle.quantize, w, 1)
+    del a, w
+    tg, rows = gemm_slab(ra, rw, 4096, 14336, 4096, 1, 4096, tsA=ra[3], tsB=rw[3])
+    out["nvfp4_mlp"] = {"quantize_s": tqa, "gemm_s": tg, "step_s": tqa + tg, "slab": "%d of 4096 rows of A" % rows,
+                        "weight_quantize_offline_s": tqw, "flop": gemm_flops(4096, 14336, 4096)}
+    del ra, rw
+    # 5. MoE: the 16384 tokens quantised in full; every routed row costs the
+    #    same N x K products, so the grouped GEMM is timed on a slab of rows of
+    #    one expert (expert 0) and scaled to the 65536 routed rows
+    x = synth.mxfp4_moe_act()
+    rx, tqx = timed(oracle.quantize, x, 0)
+    w0 = synth.mxfp4_moe_weights(experts=[0])[0]
+    rw0, tqw0 = timed(oracle.quantize, w0, 0)
+    del w0
+    tg, rows = gemm_slab(rx, rw0, 16384, 5760, 2880, 0, 65536)
+    out["mxfp4_moe"] = {"quantize_s": tqx, "gemm_s": tg, "step_s": tqx + tg,
+                        "slab": "%d routed rows against expert 0, scaled to 65536" % rows,
+                        "weight_quantize_offline_s_per_expert": tqw0, "flop": gemm_flops(65536, 5760, 2880)}
+    for v in out.values():
+        v["tflop_per_s"] = round(v["flop"] / v["step_s"] / 1e12, 7)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    print(json.dumps({"threads": threads, "configs": out}))
+
+
+def cpu_baseline_all(budget_s):
+    """The oracle on every config, single-threaded and on all the host's
+    cores (OMP_NUM_THREADS, else the affinity mask), one worker process each."""
+    import subprocess
+    info = _host_info()
+    allc = int(os.environ.get("OMP_NUM_THREADS") or info["affinity_cpus"] or os.cpu_count() or 1)
+    runs = {}
+    for t in sorted({1, allc}):
+        env = dict(os.environ, OMP_NUM_THREADS=str(t))
+        sys.stderr.write("[bench] oracle on every config, %d thread(s)\n" % t)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-worker",
+                            "--oracle-budget", str(budget_s)], env=env, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("oracle worker failed:\n" + r.stderr[-2000:])
+        runs[str(t)] = json.loads(r.stdout.strip().splitlines()[-1])["configs"]
+    print(json.dumps({"kind": "oracle", "host": info, "threads_all": allc, "runs": runs}))
+
+
 def nvfp4_decode(torch, fp4, synth, M):
     N = K = 8192
     w = synth.nvfp4_decode_weight()
@@ -543,6 +675,11 @@ def parse():
                    help="seconds of untimed steps before each workload's warm-up (clock ramp)")
     p.add_argument("--telemetry-s", type=float, default=2.5,
                    help="seconds of headline steps sampled for clock and power after the timed ones (0: none)")
+    p.add_argument("--cpu-baseline-all", action="store_true",
+                   help="only time the CPU oracle on every config, single-threaded and on all cores")
+    p.add_argument("--oracle-worker", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--oracle-budget", type=float, default=4.0,
+                   help="seconds per oracle GEMM slab in --cpu-baseline-all")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 256 MiB device copy (x*1 -> y) 3 times, to scale the HBM byte counters")
     return p.parse_args()
@@ -561,6 +698,12 @@ def calibrate_copy(torch):
 
 def main():
     args = parse()
+    if args.oracle_worker:
+        oracle_worker(args.oracle_budget)
+        return
+    if args.cpu_baseline_all:
+        cpu_baseline_all(args.oracle_budget)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this library runs on a single MI355X and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

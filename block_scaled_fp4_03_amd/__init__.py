@@ -13,7 +13,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfp4.so")
+# FP4_LIB_PATH selects another build of the same library (the tests use it
+# for the host-sanitized build); the default is the in-tree libfp4.so.
+LIB_PATH = os.environ.get("FP4_LIB_PATH") or os.path.join(HERE, "libfp4.so")
 
 # enum fp4_fmt / fp4_dtype / fp4_op, flags
 MXFP4, NVFP4, MXFP4_OCP, MXFP8, MXFP8_OCP = 0, 1, 2, 3, 4

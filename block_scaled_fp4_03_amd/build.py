@@ -64,5 +64,36 @@ def build(verbose=False):
     return OUT
 
 
+def build_sanitized(verbose=False):
+    """A host-sanitized copy of the library for the CPU test of the ABI's
+    validation paths: abi.cpp compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code only (each sanitizer flag
+    behind -Xarch_host; the kernels are the normal objects of build()).  The
+    sanitizer runtime is not linked in: a process that loads this library
+    preloads clang's libclang_rt.asan (see tests/test_sanitizers.py).
+    Returns the library's path."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, s + ".o")) for s in SOURCES):
+        build()
+    san_dir = os.path.join(BUILD_DIR, "sanitize")
+    os.makedirs(san_dir, exist_ok=True)
+    obj = os.path.join(san_dir, "abi.cpp.o")
+    host = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+    cmd = [_hipcc(), "-x", "hip"] + COMMON + host + ["-c", os.path.join(CSRC, "abi.cpp"), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("sanitized abi.cpp failed:\n" + res.stdout + res.stderr)
+    out = os.path.join(san_dir, "libfp4_san.so")
+    objs = [obj] + [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s != "abi.cpp"]
+    res = subprocess.run([_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", out] + objs,
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + res.stdout + res.stderr)
+    if verbose:
+        print("built", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -34,8 +34,29 @@ DT_F32, DT_BF16 = 0, 1
 _lib = None
 
 
+# ORACLE_SANITIZE=1 loads a copy built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (clang, no OpenMP) instead; the process must
+# preload clang's ASan runtime (tests/test_sanitizers.py does).
+LIB_SAN = os.path.join(HERE, "liboracle_san.so")
+SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build_sanitized(force=False):
+    if force or not os.path.exists(LIB_SAN) or os.path.getmtime(LIB_SAN) < os.path.getmtime(SRC):
+        tmp = LIB_SAN + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            [CLANG, "-O1", "-g", "-fno-fast-math", "-ffp-contract=off", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-shared-libsan", "-fPIC", "-shared",
+             "-Wall", "-Wno-unknown-pragmas", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB_SAN)
+    return LIB_SAN
+
+
 def build(force=False):
     """Compile fp4_oracle.c with gcc into liboracle.so next to it."""
+    if SANITIZE:
+        return build_sanitized(force)
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
@@ -49,7 +70,7 @@ def lib():
     global _lib
     if _lib is None:
         build()
-        L = ctypes.CDLL(LIB)
+        L = ctypes.CDLL(LIB_SAN if SANITIZE else LIB)
         P, I64, I32, D, F = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                              ctypes.c_double, ctypes.c_float)
         sig = {
