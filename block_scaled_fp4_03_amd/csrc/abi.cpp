@@ -196,6 +196,9 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
   if (!aligned(tsA, 4) || !aligned(tsB, 4)) return FP4_ERR_ALIGN;
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
   hipStream_t s = as_stream(stream);
+  if (nv && fp4::gemv_dot_applies(M, N, K)) {
+    return launched(fp4::launch_gemv_dot(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
+  }
   if (nv && fp4::gemv_bs_applies(M, N, K)) {
     return launched(fp4::launch_gemv_bs(A, sA, B, sB, tsA, tsB, C, M, N, K, out_dtype, s));
   }
@@ -257,7 +260,10 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
 int fp4_gemm_nvfp4_act_supported(int64_t M, int64_t N, int64_t K, int x_dtype) {
   if (!dtype_ok(x_dtype) || M < 1 || N < 1 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK)
     return 0;
-  return fp4::gemv_bs_applies(M, N, K) || fp4::gemv_nv_fused_applies(M, N, K, x_dtype) ? 1 : 0;
+  return fp4::gemv_dot_applies(M, N, K) || fp4::gemv_bs_applies(M, N, K) ||
+                 fp4::gemv_nv_fused_applies(M, N, K, x_dtype)
+             ? 1
+             : 0;
 }
 
 int fp4_gemm_nvfp4_act(const void* X, int x_dtype, float* x_tensor_scale, unsigned flags, const uint8_t* W,
@@ -267,14 +273,18 @@ int fp4_gemm_nvfp4_act(const void* X, int x_dtype, float* x_tensor_scale, unsign
   if ((flags & ~FP4_TS_GIVEN) != 0u) return FP4_ERR_FLAGS;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK || K % 32 != 0) return FP4_ERR_SHAPE;
   if (M == 0 || N == 0) return FP4_OK;
-  const bool bs = fp4::gemv_bs_applies(M, N, K);
-  if (!bs && !fp4::gemv_nv_fused_applies(M, N, K, x_dtype)) return FP4_ERR_SHAPE;
+  const bool dot = fp4::gemv_dot_applies(M, N, K);
+  const bool bs = !dot && fp4::gemv_bs_applies(M, N, K);
+  if (!dot && !bs && !fp4::gemv_nv_fused_applies(M, N, K, x_dtype)) return FP4_ERR_SHAPE;
   if (!C || !tsW) return FP4_ERR_NULL;
   if (K > 0 && (!X || !W || !sW)) return FP4_ERR_NULL;
   if ((flags & FP4_TS_GIVEN) && !x_tensor_scale) return FP4_ERR_NULL;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(sW, 4) || !aligned(tsW, 4) || !aligned(x_tensor_scale, 4))
     return FP4_ERR_ALIGN;
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
+  if (dot)
+    return launched(fp4::launch_gemv_dot_fused(X, x_dtype, x_tensor_scale, flags, W, sW, tsW, C, M, N, K, out_dtype,
+                                               as_stream(stream)));
   if (bs)
     return launched(fp4::launch_gemv_bs_fused(X, x_dtype, x_tensor_scale, flags, W, sW, tsW, C, M, N, K, out_dtype,
                                               as_stream(stream)));

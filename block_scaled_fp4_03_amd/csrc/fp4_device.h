@@ -194,17 +194,21 @@ __device__ __forceinline__ uint32_t pack8(const float y[8]) {
 // correctly rounded quotient (no underflow: the quotients that matter,
 // >= 0.25, have |x| >= 2^-102).  Tiny d takes the plain division.  The sign
 // is copied, so -0 stays -0.
-__device__ __forceinline__ float nv_div(float x, float d, float rd) {
+constexpr float kNvDivFastMin = 7.888609052210118e-31f;  // 2^-100
+
+// The d >= 2^-100 branch of nv_div alone (a caller with one d for many x
+// takes the branch once).
+__device__ __forceinline__ float nv_div_fast(float x, float d, float rd) {
   const float a = __builtin_fabsf(x);
-  float q;
-  if (d >= 7.888609052210118e-31f) {  // 2^-100
-    q = a * rd;
-    q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
-    q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
-  } else {
-    q = a / d;
-  }
+  float q = a * rd;
+  q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
+  q = __builtin_fmaf(__builtin_fmaf(-q, d, a), rd, q);
   return __builtin_copysignf(q, x);
+}
+
+__device__ __forceinline__ float nv_div(float x, float d, float rd) {
+  if (d >= kNvDivFastMin) return nv_div_fast(x, d, rd);
+  return __builtin_copysignf(__builtin_fabsf(x) / d, x);
 }
 
 // Two E4M3 bytes (bits 0-15 of w, or 16-31 when HI) as two FP16 values: the

@@ -71,6 +71,18 @@ hipError_t launch_gemv_nv(const uint8_t* A, const uint8_t* sA, const uint8_t* B,
                           const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                           int out_dtype, hipStream_t stream);
 
+// NVFP4 decode GEMV for M = 1 and K <= 8192 on the vector ALU, weights read
+// in whole 1 KB row pieces (gemv_nv_dot.hip); it takes precedence over the
+// kernels below and, like them, serves the pre-quantised and the
+// fused-activation calls alike, so that the two return the same bits.
+bool gemv_dot_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_dot(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* tsA,
+                           const float* tsB, void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                           hipStream_t stream);
+hipError_t launch_gemv_dot_fused(const void* X, int x_dtype, float* x_tensor_scale, unsigned flags, const uint8_t* B,
+                                 const uint8_t* sB, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
+                                 int out_dtype, hipStream_t stream);
+
 // NVFP4 decode GEMV for M <= 8 on the FP4 x FP4 matrix core with the block
 // scales applied to exact block sums (gemv_nv_blocksum.hip); when it applies
 // it serves both the pre-quantised and the fused-activation calls, so that

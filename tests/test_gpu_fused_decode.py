@@ -39,7 +39,8 @@ def _case(orc, M, N, K, x, w, out_bf16, given_ts=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 1000, 2880), (8, 333, 1024), (2, 64, 288), (4, 257, 8192),
-                                   (32, 70, 1024), (1, 64, 17440), (6, 96, 800), (8, 64, 8192), (12, 64, 512)])
+                                   (32, 70, 1024), (1, 64, 17440), (6, 96, 800), (8, 64, 8192), (12, 64, 512),
+                                   (1, 40, 8192), (2, 100, 8192), (2, 9, 32)])
 @pytest.mark.parametrize("bf16_x", [True, False])
 def test_fused_decode_matches_oracle(orc, M, N, K, bf16_x):
     x = synth.gaussian(300 + M, (M, K), every=97)
@@ -56,9 +57,11 @@ def test_fused_decode_given_tensor_scale(orc):
     _case(orc, M, N, K, x, w, out_bf16=True, given_ts=0.0017)
 
 
-def test_fused_decode_edge_values(orc):
+@pytest.mark.parametrize("rows", [(0, 1, 2, 3, 4, 5), (2, 3), (4,), (3,), (2,)])
+def test_fused_decode_edge_values(orc, rows):
     """Rows of zeros, -0, tiny blocks (subnormal and zero E4M3 scales) next to
-    large ones, values on E2M1 rounding ties."""
+    large ones, values on E2M1 rounding ties; all six rows and two of them
+    (block-sum kernel), single rows (vector-ALU kernel)."""
     M, N, K = 6, 128, 512
     x = synth.gaussian(321, (M, K))
     x[0] = 0.0
@@ -69,7 +72,8 @@ def test_fused_decode_edge_values(orc):
     x[4, 1:] = 0.0
     x[4, 0] = 3e-30                    # a single tiny value: tensor scale near FLT_MIN territory
     w = synth.gaussian(421, (N, K), std=0.02)
-    _case(orc, M, N, K, x.astype(np.float32), w, out_bf16=False)
+    x = np.ascontiguousarray(x[list(rows)].astype(np.float32))
+    _case(orc, len(rows), N, K, x, w, out_bf16=False)
 
 
 def test_fused_decode_all_zero_x(orc):

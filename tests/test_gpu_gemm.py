@@ -259,7 +259,8 @@ def test_nvfp4_mlp_every_tile(orc):
     assert_gemm_close(orc, C[:, cols], Cref, T, True, "nvfp4_mlp one column per 256-column band")
 
 
-# M <= 8 within its K reach takes the block-sum decode kernel; otherwise the
+# M = 1 with K <= 8192 takes the vector-ALU decode kernel, other M <= 8
+# within its K reach the block-sum decode kernel; otherwise the
 # FP16-decode kernel stages the activation as FP16 (M x K small), as codes
 # (larger), or it is too large for either (the tiled GEMM takes it):
 # (8, 100, 8960) is the largest FP16 staging at M = 8 (past the block-sum
@@ -283,6 +284,18 @@ def test_nvfp4_decode_gemv(orc, M, N, K, bf16_out):
                                    (7, 40, 288), (8, 257, 8192)])
 def test_nvfp4_decode_blocksum_shapes(orc, M, N, K):
     _gemm_case(orc, 1, M, N, K, False, seed=M * 7 + N + K, a_std=1.0, b_std=0.02)
+
+
+# The vector-ALU decode kernel (M = 1, K <= 8192): 16 weight rows per
+# workgroup, so ragged N ends inside a workgroup (17, 9, 1000, 33) and inside
+# a 32-row scale tile (40); K from one chunk (32) to the maximum (8192), with
+# threads past the row's chunks (K = 8160: 255 of 256 chunks; 2880: 90) and
+# many tiny workgroups (N = 300, K = 256).  M = 2 takes the block-sum kernel.
+@pytest.mark.parametrize("M,N,K", [(1, 16, 32), (1, 17, 64), (1, 9, 8192), (1, 1000, 2880), (1, 33, 8160),
+                                   (1, 40, 4096), (1, 300, 256), (1, 48, 8192), (2, 40, 8192)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_nvfp4_decode_vector_kernel_shapes(orc, M, N, K, bf16_out):
+    _gemm_case(orc, 1, M, N, K, bf16_out, seed=M * 5 + N + K, a_std=1.0, b_std=0.02)
 
 
 def test_nvfp4_decode_gemv_repeated_calls(orc):
