@@ -24,7 +24,7 @@ OP_QUANTIZE, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 TS_GIVEN = 1
 Q_SR, Q_2D = 2, 4
 # enum fp4_out / fp4_act (fp4_gemm_ex)
-OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP = 0, 1, 2, 3
+OUT_F32, OUT_BF16, OUT_MXFP4, OUT_MXFP4_OCP, OUT_NVFP4 = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
 
 FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quantize_noalloc", "fp4_quantize_sr",
@@ -61,7 +61,7 @@ def lib():
             "fp4_hadamard16": (I32, [P, I32, P, I32, I64, I64, ctypes.c_uint64, P]),
             "fp4_dequantize": (I32, [P, P, P, I32, P, I32, I64, I64, P]),
             "fp4_gemm": (I32, [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
-            "fp4_gemm_ex": (I32, [P, P, P, P, P, P, P, I32, P, P, I64, I64, I64, I32, I32, P]),
+            "fp4_gemm_ex": (I32, [P, P, P, P, P, P, P, I32, P, P, P, I64, I64, I64, I32, I32, P]),
             "fp4_gemm_grouped": (I32, [P, P, I64, P, P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, SZ, P]),
             "fp4_gemm_nvfp4_act": (I32, [P, I32, P, U32, P, P, P, P, I64, I64, I64, I32, P]),
             "fp4_gemm_nvfp4_act_supported": (I32, [I64, I64, I64, I32]),
@@ -123,8 +123,9 @@ def fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, work
     return lib().fp4_gemm(A, sA, B, sB, tsA, tsB, C, M, N, K, fmt, out_dtype, workspace, workspace_bytes, stream)
 
 
-def fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, M, N, K, fmt, out, stream):
-    return lib().fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, M, N, K, fmt, out, stream)
+def fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, C_tensor_scale, M, N, K, fmt, out, stream):
+    return lib().fp4_gemm_ex(A, sA, B, sB, tsA, tsB, bias, act, C, C_scales, C_tensor_scale, M, N, K, fmt, out,
+                             stream)
 
 
 def fp4_gemm_grouped(A, sA, A_rows, row_idx, group_off, E, B, sB, tsA, tsB, C, total_rows, N, K, fmt, out_dtype,
@@ -344,12 +345,14 @@ def gemm(a, b, out_dtype=None, out=None, ws=None, stream=None):
     return out
 
 
-def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
+def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, c_tensor_scale=None, stream=None):
     """C = act((A . B^T) * tsA * tsB + bias) in one kernel (see fp4_gemm_ex in
     include/fp4.h).  out: OUT_F32 / OUT_BF16 -> an M x N tensor; OUT_MXFP4 /
-    OUT_MXFP4_OCP -> a Quantized M x N MXFP4 matrix (the next GEMM's A).
-    bias: N float32 CUDA tensor or None.  C: optional preallocated output
-    (tensor, or Quantized for FP4 output)."""
+    OUT_MXFP4_OCP -> a Quantized M x N MXFP4 matrix (the next GEMM's A);
+    OUT_NVFP4 -> a Quantized M x N NVFP4 matrix under c_tensor_scale (a
+    1-element float32 CUDA tensor, required).  bias: N float32 CUDA tensor or
+    None.  C: optional preallocated output (tensor, or Quantized for FP4
+    output)."""
     torch = _torch()
     dev = _need_q(a, "a").codes.device
     _need_q(b, "b", dev)
@@ -358,27 +361,33 @@ def gemm_ex(a, b, bias=None, act=ACT_NONE, out=OUT_BF16, C=None, stream=None):
         raise ValueError("operands disagree on K or format")
     if bias is not None:
         _need(bias, "bias", (torch.float32,), N, dev)
-    fp4_out = out in (OUT_MXFP4, OUT_MXFP4_OCP)
+    fp4_out = out in (OUT_MXFP4, OUT_MXFP4_OCP, OUT_NVFP4)
+    ofmt = {OUT_MXFP4: MXFP4, OUT_MXFP4_OCP: MXFP4_OCP, OUT_NVFP4: NVFP4}.get(out)
+    if out == OUT_NVFP4:
+        if c_tensor_scale is None:
+            raise ValueError("OUT_NVFP4 needs c_tensor_scale (1-element float32 CUDA tensor)")
+        _need(c_tensor_scale, "c_tensor_scale", (torch.float32,), 1, dev)
     if C is None:
         if fp4_out:
-            ofmt = MXFP4 if out == OUT_MXFP4 else MXFP4_OCP
             nbytes = fp4_scale_bytes(ofmt, M, N)
             if nbytes < 0:
                 raise Fp4Error(int(nbytes), "fp4_scale_bytes")
             C = Quantized(torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
-                          torch.empty(nbytes, dtype=torch.uint8, device=dev), None, ofmt, M, N)
+                          torch.empty(nbytes, dtype=torch.uint8, device=dev),
+                          c_tensor_scale if out == OUT_NVFP4 else None, ofmt, M, N)
         else:
             C = torch.empty((M, N), dtype=torch.float32 if out == OUT_F32 else torch.bfloat16, device=dev)
     if fp4_out:
         if (C.rows, C.K) != (M, N):
             raise ValueError("C is a %d x %d matrix, the product %d x %d" % (C.rows, C.K, M, N))
         _need(C.codes, "C.codes", (torch.uint8,), M * (N // 2), dev)
-        _need(C.scales, "C.scales", (torch.uint8,), max(0, fp4_scale_bytes(MXFP4, M, N)), dev)
+        _need(C.scales, "C.scales", (torch.uint8,), max(0, fp4_scale_bytes(ofmt, M, N)), dev)
     else:
         _need_out(C, "C", (M, N), (torch.float32 if out == OUT_F32 else torch.bfloat16,), dev)
     cptr, sptr = (_ptr(C.codes), _ptr(C.scales)) if fp4_out else (_ptr(C), None)
+    tsc = _ptr(c_tensor_scale) if out == OUT_NVFP4 else None
     rc = fp4_gemm_ex(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), _ptr(a.tensor_scale),
-                     _ptr(b.tensor_scale), _ptr(bias), act, cptr, sptr, M, N, K, a.fmt, out, _stream(stream))
+                     _ptr(b.tensor_scale), _ptr(bias), act, cptr, sptr, tsc, M, N, K, a.fmt, out, _stream(stream))
     _check(rc, "fp4_gemm_ex")
     return C
 

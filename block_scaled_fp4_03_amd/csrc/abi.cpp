@@ -209,10 +209,10 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
 }
 
 int fp4_gemm_ex(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB, const float* tsA,
-                const float* tsB, const float* bias, int act, void* C, uint8_t* C_scales, int64_t M, int64_t N,
-                int64_t K, int fmt, int out, void* stream) {
+                const float* tsB, const float* bias, int act, void* C, uint8_t* C_scales,
+                const float* C_tensor_scale, int64_t M, int64_t N, int64_t K, int fmt, int out, void* stream) {
   if (!fmt_ok(fmt)) return FP4_ERR_FMT;
-  if (out < FP4_OUT_F32 || out > FP4_OUT_MXFP4_OCP) return FP4_ERR_DTYPE;
+  if (out < FP4_OUT_F32 || out > FP4_OUT_NVFP4) return FP4_ERR_DTYPE;
   if (act != FP4_ACT_NONE && act != FP4_ACT_RELU) return FP4_ERR_FLAGS;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 32 != 0) return FP4_ERR_SHAPE;
   if (K > kMaxGemmK || !scales_fit(fmt, M, K) || !scales_fit(fmt, N, K)) return FP4_ERR_SHAPE;
@@ -221,15 +221,18 @@ int fp4_gemm_ex(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uin
   if (M == 0 || N == 0) return FP4_OK;
   if (!C) return FP4_ERR_NULL;
   if (fp4_out && !C_scales) return FP4_ERR_NULL;
+  if (out == FP4_OUT_NVFP4 && !C_tensor_scale) return FP4_ERR_NULL;
   if (K > 0 && (!A || !sA || !B || !sB)) return FP4_ERR_NULL;
   const bool nv = fmt == FP4_NVFP4;
   if (nv && (!tsA || !tsB)) return FP4_ERR_NULL;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(sA, 4) || !aligned(sB, 4)) return FP4_ERR_ALIGN;
   if (!aligned(tsA, 4) || !aligned(tsB, 4) || !aligned(bias, 16)) return FP4_ERR_ALIGN;
+  if (out == FP4_OUT_NVFP4 && !aligned(C_tensor_scale, 4)) return FP4_ERR_ALIGN;
   if (fp4_out ? (!aligned(C, 16) || !aligned(C_scales, 4)) : !aligned(C, out == FP4_OUT_F32 ? 4 : 2))
     return FP4_ERR_ALIGN;
   return launched(fp4::launch_gemm_ex(nv ? FP4_NVFP4 : FP4_MXFP4, A, sA, B, sB, tsA, tsB, bias, act, C, C_scales,
-                                      M, N, K, out, as_stream(stream)));
+                                      out == FP4_OUT_NVFP4 ? C_tensor_scale : nullptr, M, N, K, out,
+                                      as_stream(stream)));
 }
 
 int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,

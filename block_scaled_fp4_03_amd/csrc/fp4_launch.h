@@ -42,11 +42,12 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
 // Tiled GEMM, MXFP4 (block-scaled FP4 matrix core) or NVFP4 (exact FP16
 // decode) (gemm.hip).
 // Dense GEMM with the full epilogue: + bias[N] (or nullptr), ReLU (act 1),
-// output 0 FP32, 1 BF16, 2 MXFP4 (ceil rule) / 3 MXFP4 (OCP rule) along N:
-// codes into C (M x N/2), scale tiles into Cs (N % 32 == 0, C 16-byte aligned).
+// output 0 FP32, 1 BF16, 2 MXFP4 (ceil rule) / 3 MXFP4 (OCP rule) / 4 NVFP4
+// under the given tensor scale *tsC, along N: codes into C (M x N/2), scale
+// tiles into Cs (N % 32 == 0, C 16-byte aligned).
 hipError_t launch_gemm_ex(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, const float* bias, int act, void* C, uint8_t* Cs,
-                          int64_t M, int64_t N, int64_t K, int out, hipStream_t stream);
+                          const float* tsC, int64_t M, int64_t N, int64_t K, int out, hipStream_t stream);
 hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                              const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                              int out_dtype, hipStream_t stream);

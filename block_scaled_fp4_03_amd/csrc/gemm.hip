@@ -211,7 +211,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
                                                      void* __restrict__ C, uint32_t M, uint32_t N, uint32_t K,
                                                      uint32_t tilesM, uint32_t tilesN, Groups gp,
                                                      const float* __restrict__ bias, uint32_t act,
-                                                     uint8_t* __restrict__ Cs) {
+                                                     uint8_t* __restrict__ Cs, const float* __restrict__ tsC) {
   static_assert(OUT < 2 || (!PERSIST && !GROUPED), "FP4 output: one tile per workgroup, dense");
   typedef typename Fmt<FMT>::S S;
   constexpr uint32_t STILE = Fmt<FMT>::STILE;
@@ -531,7 +531,71 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
               }
           }
           __syncthreads();
-          if constexpr (OUT >= 2) {
+          if constexpr (OUT == 4) {
+            // NVFP4 along N under the caller's tensor scale s_c (NVFP4 video
+            // transcript: 16-value blocks, E4M3 block scale, FP32 tensor
+            // scale; the deep dive §3.2 converts C to FP4 when asked), as
+            // fp4_quantize with a given tensor scale does for a rows x N
+            // matrix.  Item (row, j): 32-column chunks j, 2+j, 4+j, 6+j, two
+            // 16-blocks each, whose eight scale bytes are the two dwords of
+            // scale-tile lane 32j + row%32 (bytes 2s, 2s+1: chunk 2s + j).
+            // Rows past M and blocks past N get scale byte 0 (the tiles'
+            // padding) and no codes.
+            const float s_c = *tsC;
+            const uint32_t t = threadIdx.x;
+            if (t < 256u) {
+              const uint32_t lrow = t >> 1, j = t & 1u;
+              const uint32_t row = pass * 128u + lrow;
+              const uint32_t grow = cur.m0 + row;
+              const bool row_in = row < cur.rowsA;
+              uint32_t dw[2] = {0u, 0u};
+#pragma unroll 1
+              for (uint32_t sq = 0; sq < 4u; ++sq) {
+                const uint32_t chunk = 2u * sq + j, col0 = cur.n0 + 32u * chunk;
+                const bool blk_in = row_in && col0 < N;
+                float v[32];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                  const v4i w4 = *reinterpret_cast<const v4i*>(lds + lrow * LROW + 128u * chunk + 16u * (uint32_t)q);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[4 * q + e] = u2f((uint32_t)w4[e]);
+                }
+                v4i cw;
+                uint32_t pair = 0u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  float* x = v + 16 * h;
+                  float am = 0.0f;
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(x[e]));
+                  const uint32_t sb = blk_in ? e4m3_encode((am / 6.0f) / s_c) : 0u;
+                  if (sb == 0u) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) x[e] = __builtin_copysignf(0.0f, x[e]);   // x / inf
+                  } else {
+                    const float d = e4m3_value(sb) * s_c;
+                    const float rd = 1.0f / d;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) x[e] = nv_div(x[e], d, rd);
+                  }
+                  cw[2 * h] = (int)pack8(x);
+                  cw[2 * h + 1] = (int)pack8(x + 8);
+                  pair |= sb << (8 * h);
+                }
+                if (blk_in)
+                  *reinterpret_cast<v4i*>(static_cast<uint8_t*>(C) + (size_t)grow * (N / 2u) + col0 / 2u) = cw;
+                dw[sq >> 1] |= pair << (16u * (sq & 1u));
+              }
+              const uint32_t rows_pad = (M + 31u) & ~31u;
+              if (grow < rows_pad) {
+                const uint32_t KTo = (N + 255u) / 256u;
+                const size_t off = ((size_t)(grow >> 5) * KTo + cur.n0 / 256u) * 512u + (32u * j + (grow & 31u)) * 8u;
+                *reinterpret_cast<u32x2*>(Cs + off) = u32x2{dw[0], dw[1]};
+              }
+            }
+            __syncthreads();
+            continue;
+          } else if constexpr (OUT >= 2) {
             // Re-quantise the pass's 128 rows x 8 blocks of 32 columns
             // (MXFP4 along N, as fp4_quantize does for a rows x N matrix).
             // Item (row, j): blocks j, 2+j, 4+j, 6+j, whose scale bytes form
@@ -645,16 +709,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// out: 0 FP32, 1 BF16, 2 MXFP4 (ceil rule), 3 MXFP4 (OCP rule); FP4 output
-// only with one tile per workgroup.
+// out: 0 FP32, 1 BF16, 2 MXFP4 (ceil rule), 3 MXFP4 (OCP rule), 4 NVFP4 (given
+// tensor scale); FP4 output only with one tile per workgroup.
 template <int FMT, bool GROUPED, bool PERSIST, bool EPI>
 hipError_t launch(dim3 grid, int out, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                   const float* tsA, const float* tsB, void* C, uint32_t M, uint32_t N, uint32_t K, uint32_t tilesM,
                   uint32_t tilesN, const Groups& gp, const float* bias, uint32_t act, uint8_t* Cs,
-                  hipStream_t stream) {
+                  const float* tsC, hipStream_t stream) {
 #define GEMM_LAUNCH(O)                                                                                           \
   gemm_kernel<FMT, O, GROUPED, PERSIST, EPI><<<grid, dim3(512), 0, stream>>>(A, sA, B, sB, tsA, tsB, C, M, N, K, tilesM, \
-                                                                        tilesN, gp, bias, act, Cs)
+                                                                        tilesN, gp, bias, act, Cs, tsC)
   if (out == 0)
     GEMM_LAUNCH(0);
   else if (out == 1)
@@ -662,8 +726,10 @@ hipError_t launch(dim3 grid, int out, const uint8_t* A, const uint8_t* sA, const
   else if constexpr (!PERSIST && !GROUPED && EPI) {
     if (out == 2)
       GEMM_LAUNCH(2);
-    else
+    else if (out == 3)
       GEMM_LAUNCH(3);
+    else
+      GEMM_LAUNCH(4);
   } else {
     return hipErrorInvalidValue;
   }
@@ -708,7 +774,7 @@ static uint32_t tiled_grid(uint64_t tiles, int64_t K, bool persistent) {
 
 hipError_t launch_gemm_ex(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                           const float* tsA, const float* tsB, const float* bias, int act, void* C, uint8_t* Cs,
-                          int64_t M, int64_t N, int64_t K, int out, hipStream_t stream) {
+                          const float* tsC, int64_t M, int64_t N, int64_t K, int out, hipStream_t stream) {
   const uint32_t tilesM = (uint32_t)((M + BM - 1) / BM), tilesN = (uint32_t)((N + BN - 1) / BN);
   const Groups none{nullptr, nullptr, 0, 0, 0, 0};
   const uint32_t m = (uint32_t)M, n = (uint32_t)N, k = (uint32_t)K, a = (uint32_t)act;
@@ -718,25 +784,25 @@ hipError_t launch_gemm_ex(int fmt, const uint8_t* A, const uint8_t* sA, const ui
     const dim3 pgrid(tiled_grid((uint64_t)tilesM * tilesN, K, true));
     if (epi)
       return launch<kFmtNV, false, true, true>(pgrid, out, A, sA, B, sB, tsA, tsB, C, m, n, k, tilesM, tilesN, none,
-                                               bias, a, Cs, stream);
+                                               bias, a, Cs, nullptr, stream);
     return launch<kFmtNV, false, true, false>(pgrid, out, A, sA, B, sB, tsA, tsB, C, m, n, k, tilesM, tilesN, none,
-                                              nullptr, 0u, nullptr, stream);
+                                              nullptr, 0u, nullptr, nullptr, stream);
   }
   const dim3 grid(tilesM * tilesN);
   if (fmt == kFmtNV)   // FP4 output
     return launch<kFmtNV, false, false, true>(grid, out, A, sA, B, sB, tsA, tsB, C, m, n, k, tilesM, tilesN, none,
-                                              bias, a, Cs, stream);
+                                              bias, a, Cs, tsC, stream);
   if (epi)
     return launch<kFmtMX, false, false, true>(grid, out, A, sA, B, sB, tsA, tsB, C, m, n, k, tilesM, tilesN, none,
-                                              bias, a, Cs, stream);
+                                              bias, a, Cs, tsC, stream);
   return launch<kFmtMX, false, false, false>(grid, out, A, sA, B, sB, tsA, tsB, C, m, n, k, tilesM, tilesN, none,
-                                             nullptr, 0u, nullptr, stream);
+                                             nullptr, 0u, nullptr, nullptr, stream);
 }
 
 hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_t* sB,
                              const float* tsA, const float* tsB, void* C, int64_t M, int64_t N, int64_t K,
                              int out_dtype, hipStream_t stream) {
-  return launch_gemm_ex(fmt, A, sA, B, sB, tsA, tsB, nullptr, 0, C, nullptr, M, N, K, out_dtype, stream);
+  return launch_gemm_ex(fmt, A, sA, B, sB, tsA, tsB, nullptr, 0, C, nullptr, nullptr, M, N, K, out_dtype, stream);
 }
 
 size_t gemm_grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
@@ -758,7 +824,8 @@ hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_ro
   const Groups gp{row_idx, group_off, E, (uint32_t)A_rows, (size_t)N * (size_t)(K / 2), scale_stride};
   (void)fmt;
   return launch<kFmtMX, true, true, false>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)total_rows,
-                                    (uint32_t)N, (uint32_t)K, 0, tilesN, gp, nullptr, 0u, nullptr, stream);
+                                    (uint32_t)N, (uint32_t)K, 0, tilesN, gp, nullptr, 0u, nullptr, nullptr,
+                                    stream);
 }
 
 }  // namespace fp4

@@ -105,3 +105,49 @@ def assert_fp4_output_valid(orc, codes, scales, lo, hi, rows, M, N, ocp, what):
         raise AssertionError("%s: %d / %d codes outside the oracle's; at %s code %d, allowed order [%d, %d], "
                              "interval [%r, %r]" % (what, bad.sum(), bad.size, i, got[i], c_lo[i], c_hi[i],
                                                     float(lo[i]), float(hi[i])))
+
+
+def assert_nvfp4_output_valid(orc, codes, scales, lo, hi, rows, M, N, s_t, what):
+    """The NVFP4 counterpart of assert_fp4_output_valid, under the given tensor
+    scale s_t (FP32): the oracle's block byte E4M3((amax / 6) / s_t) is
+    non-decreasing in the block maximum, and its code of |x| / d (d =
+    E4M3value(byte) * s_t, FP32; a zero byte gives magnitude 0), sign copied,
+    is non-decreasing in x in signed order; so the outputs some v in
+    [lo, hi] gives are exactly those between the ends' outputs."""
+    R = len(rows)
+    st = np.float32(s_t)
+    lo32, hi32 = _f32_down(lo), _f32_up(hi)
+    absmin = np.where((lo32 <= 0) & (hi32 >= 0), np.float32(0), np.minimum(np.abs(lo32), np.abs(hi32)))
+    absmax = np.maximum(np.abs(lo32), np.abs(hi32))
+    nb = N // 16
+    amax_lo = absmin.reshape(R, nb, 16).max(axis=2).astype(np.float32)
+    amax_hi = absmax.reshape(R, nb, 16).max(axis=2).astype(np.float32)
+    sb_lo = orc.e4m3_encode((amax_lo / np.float32(6.0)) / st).astype(np.int64)
+    sb_hi = orc.e4m3_encode((amax_hi / np.float32(6.0)) / st).astype(np.int64)
+    sb = np.array([[scales[orc.scale_offset(1, M, N, int(r), b)] for b in range(nb)] for r in rows], np.int64)
+    bad = (sb < sb_lo) | (sb > sb_hi)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d / %d scale bytes outside the oracle's; block %s byte %d, allowed [%d, %d]"
+                             % (what, bad.sum(), bad.size, i, sb[i], sb_lo[i], sb_hi[i]))
+    d = (np.array([orc.e4m3_value(int(b)) for b in range(256)], np.float32)[np.repeat(sb, 16, axis=1)] * st)
+    d = d.astype(np.float32)
+    zero = np.repeat(sb == 0, 16, axis=1)
+
+    def code(x):
+        with np.errstate(divide="ignore", invalid="ignore"):
+            y = np.where(zero, np.float32(0), np.abs(x) / np.where(zero, np.float32(1), d)).astype(np.float32)
+        return _signed_order(_oracle_codes(orc, np.copysign(y, x)))
+
+    c_lo, c_hi = code(lo32), code(hi32)
+    packed = codes[rows].astype(np.int64)
+    got = np.empty((R, N), np.int64)
+    got[:, 0::2] = packed & 15
+    got[:, 1::2] = packed >> 4
+    g = _signed_order(got)
+    bad = (g < c_lo) | (g > c_hi)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d / %d codes outside the oracle's; at %s code %d, allowed order [%d, %d], "
+                             "interval [%r, %r]" % (what, bad.sum(), bad.size, i, got[i], c_lo[i], c_hi[i],
+                                                    float(lo[i]), float(hi[i])))

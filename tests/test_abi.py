@@ -186,15 +186,19 @@ def test_gemm_ex_argument_errors(L):
     g = fp4.fp4_gemm_ex
 
     def call(**kw):
-        a = dict(A=FAKE, sA=FAKE, B=FAKE, sB=FAKE, tsA=None, tsB=None, bias=None, act=0, C=FAKE, Cs=FAKE, M=64,
-                 N=64, K=256, fmt=0, out=2)
+        a = dict(A=FAKE, sA=FAKE, B=FAKE, sB=FAKE, tsA=None, tsB=None, bias=None, act=0, C=FAKE, Cs=FAKE, tsC=None,
+                 M=64, N=64, K=256, fmt=0, out=2)
         a.update(kw)
-        return g(a["A"], a["sA"], a["B"], a["sB"], a["tsA"], a["tsB"], a["bias"], a["act"], a["C"], a["Cs"], a["M"],
-                 a["N"], a["K"], a["fmt"], a["out"], None)
+        return g(a["A"], a["sA"], a["B"], a["sB"], a["tsA"], a["tsB"], a["bias"], a["act"], a["C"], a["Cs"],
+                 a["tsC"], a["M"], a["N"], a["K"], a["fmt"], a["out"], None)
 
     assert call(fmt=3) == -4
-    assert call(out=4) == -5
+    assert call(out=5) == -5
     assert call(out=-1) == -5
+    assert call(out=4) == -1            # NVFP4 output needs the caller's tensor scale
+    assert call(out=4, tsC=FAKE + 2) == -3
+    assert call(out=4, tsC=FAKE, N=48) == -2
+    assert call(out=4, tsC=FAKE, Cs=None) == -1
     assert call(act=2) == -8
     assert call(K=48) == -2             # K % 32
     assert call(N=48) == -2             # FP4 output needs N % 32 == 0
@@ -261,7 +265,7 @@ def test_gemm_scale_ranges_are_checked(L):
     big = 1 << 25      # rows: (2^25 / 32) tiles * 32 K-tiles * 256 B = 2^33 bytes of scales at K = 8192
     assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, big, 64, 8192, 0, 1, None, 0, None) == -2
     assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 64, big, 8192, 0, 1, None, 0, None) == -2
-    assert fp4.fp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, None, None, None, 0, FAKE, None, big, 64, 8192, 0, 1,
+    assert fp4.fp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, None, None, None, 0, FAKE, None, None, big, 64, 8192, 0, 1,
                            None) == -2
     assert fp4.fp4_gemm_grouped(FAKE, FAKE, big, FAKE, FAKE, 4, FAKE, FAKE, None, None, FAKE, 64, 64, 8192, 0, 1,
                                 None, 0, None) == -2

@@ -16,12 +16,14 @@ product quantised again to MXFP4 along N.
   E2M1 code, under that scale, of some value in the element's interval.
 - MXFP4 output, any data: equals fp4_gemm (FP32) -> + bias, ReLU (torch, FP32)
   -> fp4_quantize bit for bit, padding included (the unfused path, each part
-  of which is checked against the oracle elsewhere)."""
+  of which is checked against the oracle elsewhere).
+- NVFP4 output under a given tensor scale: the same three checks, with the
+  oracle's NVFP4 rule (E4M3 byte of (amax / 6) / s_t, codes of |x| / d)."""
 import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import assert_fp4_output_valid, say, to_dev, to_host
+from gpu_helpers import assert_fp4_output_valid, assert_nvfp4_output_valid, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -209,3 +211,97 @@ def test_fp4_output_full_size_8192(orc):
     lo, hi = _interval(orc, Cref, T, bias, fp4.ACT_RELU)
     assert_fp4_output_valid(orc, to_host(fused.codes), to_host(fused.scales), lo, hi, rows, n, n, False,
                             "fused fp4 8192^3")
+
+
+# ---- NVFP4 output under a given tensor scale ---------------------------------
+def _ts_dev(ts):
+    import torch
+    return torch.tensor([ts], dtype=torch.float32, device="cuda")
+
+
+def _fused_nv(qa, qb, bias, act, ts):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    M, N = qa.rows, qb.rows
+    tsd = _ts_dev(ts)
+    C = fp4.Quantized(torch.full((M, N // 2), 0xAB, dtype=torch.uint8, device="cuda"),
+                      torch.full((fp4.fp4_scale_bytes(fp4.NVFP4, M, N),), 0xAB, dtype=torch.uint8, device="cuda"),
+                      tsd, fp4.NVFP4, M, N)
+    return fp4.gemm_ex(qa, qb, bias=bias, act=act, out=fp4.OUT_NVFP4, C=C, c_tensor_scale=tsd)
+
+
+def _unfused_nv(qa, qb, bias, act, ts):
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    v = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    if bias is not None:
+        v = v + bias
+    if act == fp4.ACT_RELU:
+        v = torch.where(v > 0, v, torch.zeros_like(v))
+    return fp4.quantize(v.contiguous(), fp4.NVFP4, tensor_scale=_ts_dev(ts))
+
+
+NV_SHAPES = [(0, 300, 288, 544), (0, 33, 64, 96), (0, 520, 544, 2880), (1, 300, 288, 1024), (1, 64, 512, 512)]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", NV_SHAPES)
+@pytest.mark.parametrize("ts", [0.0021, 1.0, 2.0 ** -14])
+@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 1)])
+def test_nvfp4_output_equals_unfused_path(orc, fmt, M, N, K, ts, with_bias, act):
+    """Bit for bit against fp4_gemm (FP32) -> bias, ReLU -> fp4_quantize with
+    the same tensor scale, padding rows and blocks included; s_t = 2^-14
+    saturates most blocks at E4M3 448 and codes at 6."""
+    import torch
+    say("epilogue nvfp4 fmt=%d M=%d N=%d K=%d ts=%g bias=%s act=%d" % (fmt, M, N, K, ts, with_bias, act))
+    (qa, _), (qb, _) = _operands(orc, fmt, M, N, K, seed=7 * M + N + K)
+    bd = to_dev(_bias(N, 17)) if with_bias else None
+    fused = _fused_nv(qa, qb, bd, act, ts)
+    ref = _unfused_nv(qa, qb, bd, act, ts)
+    assert torch.equal(fused.codes, ref.codes), "codes differ from the unfused path"
+    assert torch.equal(fused.scales, ref.scales), "scale bytes differ from the unfused path"
+
+
+@pytest.mark.parametrize("fmt,M,N,K", NV_SHAPES)
+@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 1), (True, 0)])
+def test_nvfp4_output_valid_against_oracle(orc, fmt, M, N, K, with_bias, act):
+    """General data, s_t the oracle's own tensor scale of its epilogue values
+    (amax / 2688, what fp4_quantize would compute from C): every scale byte
+    and code is one the oracle gives for a value in the element's
+    acceptance interval; padding rows and blocks hold scale 0."""
+    say("epilogue nvfp4 valid fmt=%d M=%d N=%d K=%d bias=%s act=%d" % (fmt, M, N, K, with_bias, act))
+    (qa, ra), (qb, rb) = _operands(orc, fmt, M, N, K, seed=7 * M + N + K)
+    bias = _bias(N, 17) if with_bias else None
+    Cref, T = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, fmt, tsA=ra[3], tsB=rb[3])
+    v = orc.epilogue(Cref, bias, act)
+    ts = float(orc.nvfp4_tensor_scale(np.float32(np.abs(v).max())))
+    fused = _fused_nv(qa, qb, None if bias is None else to_dev(bias), act, ts)
+    lo, hi = _interval(orc, Cref, T, bias, act)
+    codes, scales = to_host(fused.codes), to_host(fused.scales)
+    assert_nvfp4_output_valid(orc, codes, scales, lo, hi, np.arange(M), M, N, ts, "fused nvfp4 out")
+    rows_pad = (M + 31) // 32 * 32
+    KT = (N + 255) // 256
+    pad = [orc.scale_offset(1, M, N, r, b) for r in range(M, rows_pad) for b in range(KT * 16)]
+    pad += [orc.scale_offset(1, M, N, r, b) for r in range(M) for b in range(N // 16, KT * 16)]
+    if pad:
+        assert (scales[np.array(pad, np.int64)] == 0).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 288, 512), (40, 96, 1024)])
+@pytest.mark.parametrize("ts,act", [(0.01, 1), (0.37, 0), (2.0 ** -10, 1)])
+def test_nvfp4_output_exact_against_oracle(orc, M, N, K, ts, act):
+    """Exact-sum data (every partial sum exact in FP32): the output equals the
+    oracle's NVFP4 quantisation of its epilogue value, with the same tensor
+    scale, bit for bit."""
+    import block_scaled_fp4_03_amd as fp4
+    say("epilogue nvfp4 exact M=%d N=%d K=%d ts=%g act=%d" % (M, N, K, ts, act))
+    a, b = _grid_matrix(4, M, K), _grid_matrix(5, N, K)
+    qa, ra = _quant(orc, a, fp4.MXFP4)
+    qb, rb = _quant(orc, b, fp4.MXFP4)
+    g = synth.rng(6)
+    bias = (g.integers(-64, 64, N) * 0.25).astype(np.float32)
+    fused = _fused_nv(qa, qb, to_dev(bias), act, ts)
+    Cref, _ = orc.gemm(ra[0], ra[1], rb[0], rb[1], M, N, K, orc.FMT_MXFP4)
+    v = orc.epilogue(Cref, bias, act)
+    codes, scales, _, _ = orc.quantize(v, orc.FMT_NVFP4, tensor_scale=ts)
+    np.testing.assert_array_equal(to_host(fused.codes), codes)
+    np.testing.assert_array_equal(to_host(fused.scales), scales)
