@@ -237,14 +237,19 @@ int fp4_hadamard16(const void* x, int in_dtype, void* y, int out_dtype, int64_t 
                    void* stream);
 
 /* Dequantise codes + scales (+ NVFP4 tensor scale) to a rows x K matrix of
- * `out_dtype`.  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,
+ * `out_dtype` (value = E2M1 code x block scale, x tensor scale for NVFP4:
+ * Ultralytics glossary "FP4", "How FP4 works"; "Rubin FP4 GEMM deep dive"
+ * §3.1; NVFP4 video transcript).  MXFP4 values are exact; NVFP4 computes (E2M1 * E4M3), exact,
  * times tensor_scale with one FP32 rounding; BF16 output is the round-to-
  * nearest-even of that FP32 value.  MXFP8 values are exact.  Same alignment
  * rules as fp4_quantize. */
 int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const float* tensor_scale, int fmt,
                    void* out, int out_dtype, int64_t rows, int64_t K, void* stream);
 
-/* C[M x N] = (sum_k A[m,k] * B[n,k]) * tsA * tsB, accumulated in FP32.
+/* C[M x N] = (sum_k A[m,k] * B[n,k]) * tsA * tsB, accumulated in FP32
+ * ("Rubin FP4 GEMM deep dive" §3.1-§3.2, §4.2: products of the block-scaled
+ * FP4 operands, FP32 accumulation, the scales applied to the result; §4.4 the
+ * interface; §1.2, §6.2 decode streams the weights).
  *   A: M x K quantised (codes + scales), B: N x K quantised (each row of B is one
  *   output column, i.e. B is the weight matrix stored K-contiguous).
  *   tsA, tsB: device FP32 tensor scales; required for NVFP4, optional (NULL = 1)
@@ -252,10 +257,12 @@ int fp4_dequantize(const uint8_t* codes, const uint8_t* block_scales, const floa
  *   MXFP4 runs on the gfx950 block-scaled FP4 matrix core with the E8M0 scales
  *   applied inside the instruction; NVFP4 decodes E2M1 * E4M3 exactly to FP16
  *   and runs the FP16 matrix core, with the tensor scales in the epilogue.
- *   NVFP4 with M <= 32 (decode shapes) takes a bandwidth-first path: one
- *   workgroup per 32 weight rows, K split over its wavefronts and summed in a
- *   fixed order (results do not depend on timing); no workspace.  For
- *   M <= 8 the FP4 x FP4 matrix core forms each pair of 16-value blocks'
+ *   NVFP4 with M <= 32 (decode shapes) takes a bandwidth-first path with
+ *   sums in a fixed order (results do not depend on timing) and no workspace.
+ *   M = 1 with K <= 8192 runs on the vector ALU (16 weight rows per
+ *   workgroup, each thread one 32-value chunk of every row, exact block sums
+ *   from FP16 dot products); otherwise one workgroup per 32 weight rows, K
+ *   split over its wavefronts.  For M <= 8 the FP4 x FP4 matrix core forms each pair of 16-value blocks'
  *   exact dot product and the E4M3 scales multiply those block sums in FP32
  *   (K up to 8192 at M = 5..8, 16384 at M = 2..4, 32768 at M = 1); otherwise
  *   the weights are decoded to FP16 while the activation fits the
