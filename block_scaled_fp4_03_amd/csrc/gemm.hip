@@ -137,12 +137,21 @@ struct Groups {
   size_t b_scales_stride;    // bytes between experts' scale buffers
 };
 
+// A load of read-only memory at a uniform address through the scalar cache.
+// The kernels never write the arrays read this way; without the constant
+// address space the compiler falls back to vector loads once the kernel has
+// stored anything, and those wait behind every operand copy in flight.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Rows [lo, hi) of expert e, clamped so that 0 <= lo <= hi <= total: a
 // malformed group_off (negative, decreasing or past the end) can then only
 // drop rows, never address rows of C past the end.
 __device__ __forceinline__ void group_rows(const Groups& gp, int32_t e, uint32_t total, uint32_t& lo,
                                            uint32_t& hi) {
-  const int32_t a = gp.group_off[e], b = gp.group_off[e + 1];
+  const int32_t a = sload(gp.group_off + e), b = sload(gp.group_off + e + 1);
   lo = a < 0 ? 0u : ((uint32_t)a < total ? (uint32_t)a : total);
   hi = b < 0 ? 0u : ((uint32_t)b < total ? (uint32_t)b : total);
   if (hi < lo) hi = lo;
@@ -150,12 +159,19 @@ __device__ __forceinline__ void group_rows(const Groups& gp, int32_t e, uint32_t
 
 // Locate tile t in the grouped list: tiles of expert e are ceil(cnt_e / BM)
 // m-tiles x tilesN n-tiles, ordered expert by expert.  Returns false past the
-// last tile.  Uniform per workgroup (scalar loads of group_off).
+// last tile.  Uniform per workgroup (scalar loads of group_off).  The search
+// starts at the cursor (ecur, fcur) = (expert, its first tile) of the last
+// call, since a workgroup's tiles only increase; t below the cursor restarts
+// it from expert 0.
 __device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t total_rows, uint32_t t, uint32_t tilesN,
                                              uint32_t& e_out, uint32_t& row0, uint32_t& rows, uint32_t& tm,
-                                             uint32_t& tn) {
-  uint32_t first = 0;
-  for (int32_t e = 0; e < gp.E; ++e) {
+                                             uint32_t& tn, int32_t& ecur, uint32_t& fcur) {
+  if (t < fcur) {
+    ecur = 0;
+    fcur = 0;
+  }
+  uint32_t first = fcur;
+  for (int32_t e = ecur; e < gp.E; ++e) {
     uint32_t lo, hi;
     group_rows(gp, e, total_rows, lo, hi);
     const uint32_t cnt = hi - lo;
@@ -169,6 +185,8 @@ __device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t total_ro
       rows = cnt;
       tm = a;
       tn = b;
+      ecur = e;
+      fcur = first;
       return true;
     }
     first += n;
@@ -257,13 +275,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
   for (int q = 0; q < 4; ++q) voffB[q] = (8u * (wave + 8u * q) + grow) * ldb + 16u * gchunk;
 
+  int32_t g_ecur = 0;     // grouped: search cursor of grouped_tile
+  uint32_t g_fcur = 0;
   auto make_tile = [&](uint32_t t, TileAddr& T) {
     uint32_t rowsA, row0 = 0, expert = 0, m0, n0;
     const uint8_t* Bx = B;
     const uint8_t* sBx = sB;
     if (GROUPED) {
       uint32_t cnt, tm, tn;
-      grouped_tile(gp, M, t, tilesN, expert, row0, cnt, tm, tn);
+      grouped_tile(gp, M, t, tilesN, expert, row0, cnt, tm, tn, g_ecur, g_fcur);
       m0 = tm * BM;
       n0 = tn * BN;
       rowsA = (cnt - m0) < BM ? (cnt - m0) : BM;
@@ -291,20 +311,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       // the group get an out-of-range offset and load zeros.
       T.a_base = A;
       T.a_bytes = gp.A_rows * ldb;
+      // The token indices (rows past the group read the tile's first row);
+      // turned into offsets by gather_offsets.
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t r = 8u * (wave + 8u * q) + grow;
-        T.voffA[q] = r < rowsA ? (uint32_t)gp.row_idx[row0 + m0 + r] * ldb + 16u * gchunk : 0x80000000u;
+        T.voffA[q] = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
       }
-      // Scale dwords: lane L = 32j + i of scale block `wave` is row i, chunk
-      // parity j, found at the gathered row's own scale tile.
-      const uint32_t i = lane & 31u, r = 32u * wave + i;
-      if (r < rowsA) {
-        const uint32_t tok = (uint32_t)gp.row_idx[row0 + m0 + r];
-        T.svoffA = (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u;
-      } else {
-        T.svoffA = 0x80000000u;
-      }
+      const uint32_t r = 32u * wave + (lane & 31u);
+      T.svoffA = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
       T.sa_base = sA;
       T.sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
     } else {
@@ -315,6 +330,21 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       T.sa_base = sA + (size_t)(m0 / 32u) * srow;
       T.sa_bytes = (RTA > m0 / 32u ? RTA - m0 / 32u : 0u) * srow;
     }
+  };
+
+  // Grouped: the loaded token indices of T become its lane offsets; rows
+  // past the group get an out-of-range offset and load zeros.  Scale dwords:
+  // lane L = 32j + i of scale block `wave` is row i, chunk parity j, found at
+  // the gathered row's own scale tile.
+  auto gather_offsets = [&](TileAddr& T) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = 8u * (wave + 8u * q) + grow;
+      T.voffA[q] = r < T.rowsA ? T.voffA[q] * ldb + 16u * gchunk : 0x80000000u;
+    }
+    const uint32_t tok = T.svoffA;
+    T.svoffA = 32u * wave + (lane & 31u) < T.rowsA ? (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u
+                                                   : 0x80000000u;
   };
 
   // Copy stage `stage_k` of tile T into LDS buffer `buf`; stages past K (or
@@ -379,6 +409,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   if (!tile_of(v, t)) return;
   TileAddr cur;
   make_tile(t, cur);
+  if (GROUPED) gather_offsets(cur);
   const float scale = (tsA ? *tsA : 1.0f) * (tsB ? *tsB : 1.0f);
 
   // Stage k of a tile covers K values [256k, 256k + 256) in four 64-value
@@ -438,6 +469,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // The next tile's token indices, loaded at the tile's start, have
+      // arrived with this wait: a wait right after their loads would also
+      // wait for the previous tile's C stores (loads and stores retire in
+      // order), about 2.6 us per tile.
+      if (GROUPED && k == 0u && has_next) gather_offsets(nxt);
       // Stage g+k+2 goes into this buffer: this tile's stage k+2, or the next
       // tile's stage k+2-KT.
       const bool own = k + 2u < KT;
