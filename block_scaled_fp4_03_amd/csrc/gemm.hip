@@ -714,23 +714,35 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       const uint32_t lrow0 = 128u * wm + 4u * lj;                 // this lane's first row in the tile
       const uint32_t lcol0 = cur.n0 + 64u * wn + li;              // this lane's first column
       const size_t lbase = ((size_t)cur.row0 + cur.m0 + lrow0) * Nu + lcol0;
+      auto store = [&](int r, int i, int c) {
+        const uint32_t rr = 32u * r + 8u * (i >> 2) + (i & 3);  // row offset from lrow0
+        const float val = epi(acc[r][c][i], c);
+        const size_t e = lbase + (size_t)rr * Nu + 32u * c;
+        if (OUT == 0)
+          static_cast<float*>(C)[e] = val;
+        else
+          static_cast<uint16_t*>(C)[e] = f32_to_bf16(val);
+      };
+      // A whole tile stores without per-element masks: a masked store is a
+      // branch of its own (exec mask saved, tested and restored), and those
+      // made up most of the epilogue's instructions.
+      if (cur.rowsA == BM && cur.n0 + BN <= N) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t rr = 32u * r + 8u * (i >> 2) + (i & 3);  // row offset from lrow0
-          const size_t roff = (size_t)rr * Nu;
-          const bool row_ok = lrow0 + rr < cur.rowsA;
+          for (int i = 0; i < 16; ++i)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            if (row_ok && lcol0 + 32u * c < N) {
-              const float val = epi(acc[r][c][i], c);
-              const size_t e = lbase + roff + 32u * c;
-              if (OUT == 0)
-                static_cast<float*>(C)[e] = val;
-              else
-                static_cast<uint16_t*>(C)[e] = f32_to_bf16(val);
-            }
+            for (int c = 0; c < 2; ++c) store(r, i, c);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t rr = 32u * r + 8u * (i >> 2) + (i & 3);
+            const bool row_ok = lrow0 + rr < cur.rowsA;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              if (row_ok && lcol0 + 32u * c < N) store(r, i, c);
           }
         }
       }

@@ -531,3 +531,42 @@ def test_wrapper_rejects_int64_group_offsets():
     with pytest.raises(ValueError, match="contiguous"):
         fp4.gemm_grouped(qa, torch.arange(20, device="cuda", dtype=torch.int32)[::2], off.int(), codes, scales,
                          64, 64, 0)
+
+
+def _rne_bf16_of(c32):
+    """torch's (CPU) round-to-nearest-even of FP32 values to BF16, as bits."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(c32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("path", ["dense_mx", "dense_nv", "grouped", "grouped_partial"])
+def test_bf16_output_is_rne_of_fp32_output(orc, path):
+    """The same call with BF16 and with FP32 output forms the same FP32 sums,
+    so every BF16 element must be the round-to-nearest-even of the FP32 one,
+    bit for bit: this pins each epilogue's BF16 rounding (through LDS in the
+    one-tile-per-workgroup kernel, from registers in the persistent ones, on
+    their unmasked whole-tile path and their masked partial-tile path)."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    if path in ("dense_mx", "dense_nv"):
+        fmt = 0 if path == "dense_mx" else 1
+        M, N, K = (520, 512, 1024) if fmt == 0 else (600, 520, 1024)
+        say("bf16 rne %s M=%d N=%d K=%d" % (path, M, N, K))
+        qa = fp4.quantize(to_dev(synth.gaussian(301 + fmt, (M, K))), fmt)
+        qb = fp4.quantize(to_dev(synth.gaussian(311 + fmt, (N, K), std=0.05)), fmt)
+        c32 = to_host(fp4.gemm(qa, qb, out_dtype=torch.float32))
+        c16 = to_host(fp4.gemm(qa, qb, out_dtype=torch.bfloat16))
+    else:
+        counts = np.array([512, 3, 260, 0, 256] if path == "grouped" else [40, 300, 1])
+        N, K = (512, 1024) if path == "grouped" else (300, 544)
+        T_rows = 600
+        row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=int(counts.sum()) + N)
+        say("bf16 rne %s counts=%s N=%d K=%d" % (path, counts.tolist(), N, K))
+        qa = fp4.quantize(to_dev(synth.to_bf16_bits(synth.gaussian(321, (T_rows, K)))), 0)
+        ws = [synth.gaussian(330 + e, (N, K), std=0.02) for e in range(counts.size)]
+        codes, scales, _ = _quant_experts(orc, ws, 0)
+        ri, go = torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda()
+        c32 = to_host(fp4.gemm_grouped(qa, ri, go, codes, scales, N, K, 0, out_dtype=torch.float32))
+        c16 = to_host(fp4.gemm_grouped(qa, ri, go, codes, scales, N, K, 0, out_dtype=torch.bfloat16))
+    assert np.isfinite(c32).all() and np.abs(c32).max() > 0
+    np.testing.assert_array_equal(c16.view(np.uint16), _rne_bf16_of(c32))
