@@ -37,8 +37,9 @@
 // n (bytes 256u + 32g + 16h: step g's K half h) and its 8 scale bytes in each
 // of the tiles 2u and 2u + 1.  When step g of a unit has gone to the matrix
 // core, the same registers receive step g of the wave's next unit, so the
-// weights stream without a pause.  The activation is staged once per
-// workgroup in LDS as 16-byte operand slots (a block's 8 code bytes in the
+// weights stream without a pause.  The activation is staged in LDS (by each
+// wave for the units it reads, or, when X is quantised in the kernel, by the
+// whole workgroup) as 16-byte operand slots (a block's 8 code bytes in the
 // half of the slot its K half needs, zeros in the other) plus its block
 // scales in FP32.  The 16 waves' sums are added in a fixed order through LDS
 // at the end of each row block: the result is deterministic, and the fused
@@ -114,15 +115,24 @@ __global__ __launch_bounds__(BS_WAVES * 64, 1) void gemv_bs_kernel(
   v4i xl[NX][NXL];
   v4i ald[NC];
   uint32_t asc[NC];
+  // Codes: each wave stages the units it reads (u = wave + 16 j), so that it
+  // starts without waiting for the rest of the workgroup.  Its chunk q =
+  // lane + 64 i is 32 values (blocks 2cu, 2cu + 1) of row m of unit u:
+  // j = q / 16MB, then m = q % MB, cu = 16 u + (q % 16MB) / MB.
+  auto own_chunk = [&](int i, uint32_t& m, uint32_t& cu) {
+    const uint32_t q = lane + 64u * (uint32_t)i, j = q / (16u * MB), r = q % (16u * MB);
+    m = r % MB;
+    cu = 16u * (wave + BS_WAVES * j) + r / MB;
+    return j < NJ;
+  };
   if (!FUSED) {
-    // Chunk c = 32 values (blocks 2cu, 2cu + 1) of row m = c % MB, cu = c / MB.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, M * ldb);
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sA, srow);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const uint32_t c = tid + 1024u * i;
-      const uint32_t m = c % MB, cu = c / MB;
-      const bool ok = m < M && 32u * cu < K;
+      uint32_t m, cu;
+      const bool mine = own_chunk(i, m, cu);
+      const bool ok = mine && m < M && 32u * cu < K;
       ald[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? m * ldb + 16u * cu : 0x80000000u,
                                                                             0, 0));
       asc[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, ok ? scale_offset<kFmtNV>(m, 2u * cu, KT) : 0x80000000u, 0, 0);
@@ -191,9 +201,8 @@ __global__ __launch_bounds__(BS_WAVES * 64, 1) void gemv_bs_kernel(
   if (!FUSED) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const uint32_t c = tid + 1024u * i;
-      const uint32_t m = c % MB, cu = c / MB;
-      if (cu < NU * 16u) {
+      uint32_t m, cu;
+      if (own_chunk(i, m, cu) && cu < NU * 16u) {
         const uint32_t u = cu >> 4, bl = 2u * (cu & 15u);
         uint8_t* ub = lds + u * G::UNIT_BYTES;
         *reinterpret_cast<v4i*>(ub + (bl * MB + m) * 16u) = v4i{ald[i][0], ald[i][1], 0, 0};
@@ -288,10 +297,16 @@ __global__ __launch_bounds__(BS_WAVES * 64, 1) void gemv_bs_kernel(
       }
     }
   }
-  if (tid < NU) *reinterpret_cast<v4i*>(lds + tid * G::UNIT_BYTES + G::ZSLOT) = v4i{};
-  __syncthreads();
+  if (FUSED) {
+    if (tid < NU) *reinterpret_cast<v4i*>(lds + tid * G::UNIT_BYTES + G::ZSLOT) = v4i{};
+    __syncthreads();
+  } else if (lane < NJ && wave + BS_WAVES * lane < NU) {
+    // this wave's units' zero slots (LDS operations of one wave complete in
+    // order: its own reads below see them)
+    *reinterpret_cast<v4i*>(lds + (wave + BS_WAVES * lane) * G::UNIT_BYTES + G::ZSLOT) = v4i{};
+  }
   // The rest of the first unit's weight steps, requested once the
-  // workgroup's activation is staged.  Requested earlier, they queue behind
+  // activation is staged (codes: this wave's units).  Requested earlier, they queue behind
   // the whole grid's weight stream and delay the activation's own loads (at
   // 8192 x 8192, M = 1: all 8 steps first 10.3 us, 4 first 9.7 us; waves that
   // request the rest as soon as their own share has arrived 10.4 us).
@@ -414,8 +429,8 @@ int bs_mb(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 template <int MB>
 bool bs_fits(int64_t K) {
   using G = BsGeom<MB>;
-  const int64_t nu = (K + 511) / 512;
-  return MB * nu * 32 <= 1024 * (int64_t)G::XNB &&
+  const int64_t nu = (K + 511) / 512, nj = nu > BS_WAVES ? (nu + BS_WAVES - 1) / BS_WAVES : 1;
+  return MB * nu * 32 <= 1024 * (int64_t)G::XNB && 16 * MB * nj <= 64 * (int64_t)G::NA &&
          nu * (int64_t)G::UNIT_BYTES + (int64_t)G::RED_BYTES <= (int64_t)BS_LDS_BYTES;
 }
 
