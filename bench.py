@@ -539,7 +539,9 @@ def nvfp4_decode(torch, fp4, synth, M):
     # quantise + GEMM step at small M only (measured: M = 1 11.6 vs 14.3 us,
     # M = 2 12.4 vs 14.0 us, M = 4 16.9 vs 14.6 us).
     fused = M <= 2 and bool(fp4.fp4_gemm_nvfp4_act_supported(M, N, K, fp4.BF16))
-    small_x = M * K * 2 <= 256 * 1024   # fp4_quantize's one-launch NVFP4 path (tensors up to 256 KB)
+    # fp4_quantize's NVFP4 paths: one launch up to 256 KB (every workgroup
+    # reduces the maximum) and up to 1 MB (workgroups exchange it), two above
+    one_launch_q = M * K * 2 <= 1024 * 1024
     if fused:
         # one kernel: tensor amax + NVFP4 quantise of X + GEMV
         def step(i):
@@ -569,7 +571,7 @@ def nvfp4_decode(torch, fp4, synth, M):
     return {"M": M, "N": N, "K": K, "us_per_step": round(ms * 1e3, 3), "algorithmic_bytes": int(nbytes),
             "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "step": ("one kernel: tensor amax + NVFP4 quantise of X + decode GEMV" if fused else
-                     ("two kernels: one-launch tensor amax + NVFP4 quantise of X, decode GEMV" if small_x else
+                     ("two kernels: one-launch tensor amax + NVFP4 quantise of X, decode GEMV" if one_launch_q else
                       "three kernels: tensor amax, NVFP4 quantise of X, decode GEMV")) + " (HIP graph replay)"}
 
 

@@ -60,7 +60,7 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K) {
 size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int32_t E) {
   switch (op) {
     case FP4_OP_QUANTIZE:
-      return fmt == FP4_NVFP4 ? 8 : 0;
+      return fmt == FP4_NVFP4 ? 16 : 0;
     case FP4_OP_GEMM:
       return 0;
     case FP4_OP_GEMM_GROUPED:
@@ -89,13 +89,16 @@ static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_
   if (nv && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
   const bool compute_ts = nv && !(flags & FP4_TS_GIVEN);
   if (compute_ts) {
-    if (!workspace || workspace_bytes < 8) return FP4_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < 16) return FP4_ERR_WORKSPACE;
     if (!aligned(workspace, 4)) return FP4_ERR_ALIGN;
   }
   hipStream_t s = as_stream(stream);
   if (compute_ts && !twod && fp4::quantize_nv_small_applies(rows, K, in_dtype))
     return launched(
         fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
+  if (compute_ts && !twod && fp4::quantize_nv_grid_applies(rows, K, in_dtype))
+    return launched(fp4::launch_quantize_nv_grid(x, in_dtype, codes, block_scales, tensor_scale,
+                                                 static_cast<uint32_t*>(workspace), rows, K, sr, seed, 0u, s));
   if (compute_ts) {
     int rc = launched(fp4::launch_tensor_amax(x, in_dtype, rows * K, static_cast<uint32_t*>(workspace), tensor_scale, s));
     if (rc != FP4_OK) return rc;

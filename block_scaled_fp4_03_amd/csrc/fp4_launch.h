@@ -25,6 +25,13 @@ bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype);
 hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
                                     float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,
                                     hipStream_t stream);
+// NVFP4 with its own tensor scale in one launch for inputs above 256 KB and
+// at most 1 MB: workgroups exchange the maximum through ws (3 words, zero
+// before the call and after it).  spin_limit 0 takes the default wait.
+bool quantize_nv_grid_applies(int64_t rows, int64_t K, int in_dtype);
+hipError_t launch_quantize_nv_grid(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                   float* tensor_scale, uint32_t* ws, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                   uint32_t spin_limit, hipStream_t stream);
 // NVFP4 with 16 x 16 patch scales (tensor scale already in *tensor_scale).
 hipError_t launch_quantize_nv2d(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
                                 const float* tensor_scale, int64_t rows, int64_t K, bool sr, uint64_t seed,

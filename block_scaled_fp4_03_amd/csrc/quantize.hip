@@ -392,30 +392,13 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const void* __restrict
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNvSmallMaxBytes = 256u * 1024u;
 
-template <int DT, bool SR>
-__global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __restrict__ x,
-                                                                 uint8_t* __restrict__ codes,
-                                                                 uint8_t* __restrict__ scales,
-                                                                 float* __restrict__ tensor_scale, size_t n8,
-                                                                 uint32_t rows, uint32_t K, uint32_t KT,
-                                                                 uint32_t KT2, uint32_t total_waves, uint64_t seed) {
-  __shared__ float red[16];
-  const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+// This thread's share of the whole tensor's largest magnitude (n8 chunks of 8
+// values): loads in batches of 8 chunks per thread, all issued before their
+// use; buffer loads past the end return zeros (no branch, so the batch stays
+// in flight together).  fmaxf skips NaNs.
+template <int DT>
+__device__ __forceinline__ float whole_tensor_max(__amdgpu_buffer_rsrc_t rx, size_t n8, uint32_t tid) {
   constexpr uint32_t EB = DT == kDtF32 ? 4u : 2u;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)(n8 * 8u * EB));
-  // This wave's own values first (they arrive while the maximum is reduced);
-  // branch-free, so that nothing waits for them before the loads below.
-  const uint32_t wave = blockIdx.x * 16u + w;
-  const uint32_t row = wave / KT2, k0 = (wave % KT2) * 512u + lane * 8u;
-  const bool valid = wave < total_waves && row < rows && k0 < K;
-  const uint32_t voff = valid ? (row * K + k0) * EB : 0x80000000u;
-  u32x4 own[EB / 2u];
-#pragma unroll
-  for (uint32_t h = 0; h < EB / 2u; ++h)
-    own[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + 16u * h, 0, 0));
-  // Loads in batches of 8 chunks (of 8 values) per thread, all issued before
-  // their use; at most 256 KB means at most 2 batches.  Buffer loads past the
-  // end return zeros (no branch, so the batch stays in flight together).
   float m = 0.0f;
   for (uint32_t b = tid; b < (uint32_t)n8; b += 8u * 1024u) {
     u32x4 raw[8][EB / 2u];
@@ -440,6 +423,32 @@ __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __r
           }
         }
   }
+  return m;
+}
+
+template <int DT, bool SR>
+__global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __restrict__ x,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales,
+                                                                 float* __restrict__ tensor_scale, size_t n8,
+                                                                 uint32_t rows, uint32_t K, uint32_t KT,
+                                                                 uint32_t KT2, uint32_t total_waves, uint64_t seed) {
+  __shared__ float red[16];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+  constexpr uint32_t EB = DT == kDtF32 ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)(n8 * 8u * EB));
+  // This wave's own values first (they arrive while the maximum is reduced);
+  // branch-free, so that nothing waits for them before the loads below.
+  const uint32_t wave = blockIdx.x * 16u + w;
+  const uint32_t row = wave / KT2, k0 = (wave % KT2) * 512u + lane * 8u;
+  const bool valid = wave < total_waves && row < rows && k0 < K;
+  const uint32_t voff = valid ? (row * K + k0) * EB : 0x80000000u;
+  u32x4 own[EB / 2u];
+#pragma unroll
+  for (uint32_t h = 0; h < EB / 2u; ++h)
+    own[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + 16u * h, 0, 0));
+  // At most 256 KB: at most 2 batches per thread.
+  float m = whole_tensor_max<DT>(rx, n8, tid);
   m = wave_fmax(m);
   if (lane == 0u) red[w] = m;
   __syncthreads();
@@ -463,6 +472,110 @@ __global__ __launch_bounds__(1024) void quantize_nv_small_kernel(const void* __r
       v[2 * k + 1] = u2f(own[0][k] & 0xFFFF0000u);
     }
   }
+  if (wave < total_waves) quantize_nv_wave<SR>(v, valid, codes, scales, s_t, K, KT, KT2, wave, lane, seed);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantiser for mid-size tensors (above 256 KB, at most 1 MB: e.g. a
+// 32-row decode activation), one launch without re-reading the tensor: each
+// workgroup of 16 waves loads only its own 512-value pieces, folds their
+// maximum into the workspace's running maximum (device-scope atomics, as
+// tensor_amax_kernel) and counts itself in, waits until every workgroup has
+// counted in, reads the maximum and quantises its pieces.  Workspace words:
+// [0] the running maximum (magnitude bits), [1] workgroups counted in, [2]
+// workgroups done with the maximum; the last of those clears all three for
+// the next call.  The wait is bounded (spin_limit sleeps): a grid of at most
+// 128 workgroups is resident at once on this part, but a workgroup that stops
+// waiting reduces the whole tensor's maximum itself, which is the same exact
+// value, so the result never depends on the wait.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNvGridMaxBytes = 1024u * 1024u;
+constexpr uint32_t kNvGridSpin = 1u << 16;
+constexpr uint32_t kNoMax = 0xFFFFFFFFu;
+
+template <int DT, bool SR>
+__global__ __launch_bounds__(1024) void quantize_nv_grid_kernel(const void* __restrict__ x,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales,
+                                                                float* __restrict__ tensor_scale,
+                                                                uint32_t* __restrict__ ws, size_t n8, uint32_t rows,
+                                                                uint32_t K, uint32_t KT, uint32_t KT2,
+                                                                uint32_t total_waves, uint32_t spin_limit,
+                                                                uint64_t seed) {
+  __shared__ float red[16];
+  __shared__ uint32_t max_bits;
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+  constexpr uint32_t EB = DT == kDtF32 ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)(n8 * 8u * EB));
+  const uint32_t wave = blockIdx.x * 16u + w;
+  const uint32_t row = wave / KT2, k0 = (wave % KT2) * 512u + lane * 8u;
+  const bool valid = wave < total_waves && row < rows && k0 < K;
+  const uint32_t voff = valid ? (row * K + k0) * EB : 0x80000000u;
+  u32x4 own[EB / 2u];
+#pragma unroll
+  for (uint32_t h = 0; h < EB / 2u; ++h)
+    own[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + 16u * h, 0, 0));
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (DT == kDtF32) {
+      v[k] = u2f(own[0][k]);
+      v[4 + k] = u2f(own[EB / 2u - 1u][k]);
+    } else {
+      v[2 * k] = u2f(own[0][k] << 16);
+      v[2 * k + 1] = u2f(own[0][k] & 0xFFFF0000u);
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));   // pieces past the tensor loaded zeros
+  m = wave_fmax(m);
+  if (lane == 0u) red[w] = m;
+  __syncthreads();
+  if (tid == 0u) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i]);
+    // The max is performed before this workgroup counts itself in (wait for
+    // its return), so a workgroup that sees every count sees every max.
+    const uint32_t prev = __hip_atomic_fetch_max(&ws[0], f2u(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" : : "v"(prev) : "memory");
+    __hip_atomic_fetch_add(&ws[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t bits = kNoMax;
+    for (uint32_t it = 0; it < spin_limit; ++it) {
+      if (__hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gridDim.x) {
+        bits = __hip_atomic_load(&ws[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    max_bits = bits;
+  }
+  __syncthreads();
+  float amax;
+  if (max_bits != kNoMax) {
+    amax = u2f(max_bits);
+  } else {
+    // Stopped waiting: the whole tensor's maximum from every element.
+    float mm = wave_fmax(whole_tensor_max<DT>(rx, n8, tid));
+    if (lane == 0u) red[w] = mm;
+    __syncthreads();
+    amax = red[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) amax = fmaxf(amax, red[i]);
+  }
+  if (tid == 0u) {
+    const uint32_t done = __hip_atomic_fetch_add(&ws[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1u) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) __hip_atomic_store(&ws[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  float s_t = 1.0f;
+  if (amax > 0.0f) {
+    s_t = amax / 2688.0f;
+    if (s_t < FLT_MIN) s_t = FLT_MIN;
+  }
+  if (blockIdx.x == 0 && tid == 0) *tensor_scale = s_t;
   if (wave < total_waves) quantize_nv_wave<SR>(v, valid, codes, scales, s_t, K, KT, KT2, wave, lane, seed);
 }
 
@@ -657,6 +770,11 @@ hipError_t launch_tensor_amax(const void* x, int in_dtype, int64_t n, uint32_t* 
   return hipGetLastError();
 }
 
+bool quantize_nv_grid_applies(int64_t rows, int64_t K, int in_dtype) {
+  const int64_t bytes = rows * K * (in_dtype == kDtF32 ? 4 : 2);
+  return rows >= 1 && K >= 16 && bytes > (int64_t)kNvSmallMaxBytes && bytes <= (int64_t)kNvGridMaxBytes;
+}
+
 bool quantize_nv_small_applies(int64_t rows, int64_t K, int in_dtype) {
   const int64_t bytes = rows * K * (in_dtype == kDtF32 ? 4 : 2);
   return rows >= 1 && K >= 16 && bytes <= (int64_t)kNvSmallMaxBytes;
@@ -762,6 +880,34 @@ hipError_t launch_quantize_nv_small(const void* x, int in_dtype, uint8_t* codes,
     launch_nv_small<true>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
   else
     launch_nv_small<false>(x, in_dtype, codes, scales, tensor_scale, rows, K, seed, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nv_grid(const void* x, int in_dtype, uint8_t* codes, uint8_t* scales,
+                                   float* tensor_scale, uint32_t* ws, int64_t rows, int64_t K, bool sr, uint64_t seed,
+                                   uint32_t spin_limit, hipStream_t stream) {
+  const uint32_t r = (uint32_t)rows, k = (uint32_t)K;
+  const uint32_t rows_pad = (r + 31u) / 32u * 32u;
+  const uint32_t KT = (k + 255u) / 256u, KT2 = (KT + 1u) / 2u;
+  const uint32_t waves = rows_pad * KT2;
+  const dim3 grid((waves + 15u) / 16u);
+  const size_t n8 = (size_t)rows * (size_t)K / 8u;
+  const uint32_t spin = spin_limit ? spin_limit : kNvGridSpin;
+#define NV_GRID(DT, SRB)                                                                                        \
+  quantize_nv_grid_kernel<DT, SRB><<<grid, dim3(1024), 0, stream>>>(x, codes, scales, tensor_scale, ws, n8, r, k, KT, \
+                                                                     KT2, waves, spin, seed)
+  if (in_dtype == kDtF32) {
+    if (sr)
+      NV_GRID(kDtF32, true);
+    else
+      NV_GRID(kDtF32, false);
+  } else {
+    if (sr)
+      NV_GRID(kDtBF16, true);
+    else
+      NV_GRID(kDtBF16, false);
+  }
+#undef NV_GRID
   return hipGetLastError();
 }
 

@@ -122,8 +122,8 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
 /* Workspace bytes an operation needs (0 if none).  For FP4_OP_QUANTIZE, M is
  * the row count; for FP4_OP_GEMM_GROUPED, E is the expert count and M the total
  * routed rows.  Today only NVFP4 quantisation that computes its own tensor
- * scale needs one (8 bytes: the running amax and a completion counter); GEMMs
- * return 0.  Operations keep their control words at the start of the
+ * scale needs one (16 bytes: the running amax and two workgroup counters);
+ * GEMMs return 0.  Operations keep their control words at the start of the
  * workspace.  A workspace must be zero-filled once before its first use; every
  * call leaves the control words zero again when its work on the stream
  * completes, so one zero-filled workspace of the largest size needed serves
@@ -149,9 +149,12 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
  *   is ignored for MXFP4.  NVFP4 without FP4_TS_GIVEN needs a workspace of
  *   fp4_workspace_size(FP4_OP_QUANTIZE, ...) bytes; otherwise workspace may be NULL.
  *   (Inputs of at most 256 KB take a single launch in which every workgroup
- *   reduces the maximum itself and the workspace is left untouched; larger ones
- *   reduce across workgroups through the workspace, then quantise.  Both give
- *   the same bits.)
+ *   reduces the maximum itself and the workspace is left untouched; up to 1 MB,
+ *   a single launch whose workgroups exchange the maximum through the
+ *   workspace and wait for each other (a bounded wait, after which a
+ *   workgroup reduces the whole maximum itself); larger ones reduce across
+ *   workgroups through the workspace, then quantise.  All give the same
+ *   bits.)
  * rows == 0 or K == 0 is a no-op. */
 int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
@@ -162,7 +165,7 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
  * Same arguments, rules, errors and bits as fp4_quantize (flags:
  * FP4_TS_GIVEN only), without the workspace: where fp4_quantize would use one
  * (NVFP4 computing its own tensor scale over more than 256 KB of input), the
- * running maximum and completion counter live in a scratch array the library
+ * running maximum and workgroup counters live in a scratch array the library
  * holds, a static device array of 256 bytes on each GPU (held until the
  * process ends).  The call allocates nothing and calls no allocating
  * routine.
@@ -175,7 +178,7 @@ int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, 
  *   and give wrong tensor scales.  Order them, or use fp4_quantize with a
  *   workspace per stream.
  * Errors: as fp4_quantize; FP4_ERR_WORKSPACE if the operation needed more
- * than the array's 256 bytes (no format needs more than 8 today);
+ * than the array's 256 bytes (no format needs more than 16 today);
  * FP4_ERR_HIP if the array cannot be located on the current device or the
  * clearing kernel fails to launch. */
 int fp4_quantize_noalloc(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,

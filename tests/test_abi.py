@@ -59,7 +59,7 @@ def test_scale_bytes_agrees_with_oracle(L, orc):
 
 def test_workspace_sizes(L):
     assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.MXFP4, 10, 0, 64) == 0
-    assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.NVFP4, 10, 0, 64) == 8
+    assert fp4.fp4_workspace_size(fp4.OP_QUANTIZE, fp4.NVFP4, 10, 0, 64) == 16
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.MXFP4, 8192, 8192, 8192) == 0
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 1, 8192, 8192) == 0
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 8192, 8192) == 0
@@ -91,6 +91,7 @@ def test_quantize_argument_errors(L):
     # NVFP4 computing its tensor scale needs the workspace
     assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 0, None, 0, None) == -6
     assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 0, FAKE, 4, None) == -6
+    assert q(FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 0, 0, FAKE, 8, None) == -6   # 16 bytes since the one-launch grid path
 
 
 def test_dequantize_argument_errors(L):

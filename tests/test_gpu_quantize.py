@@ -89,6 +89,34 @@ def test_nvfp4_single_launch_threshold(orc, rows, K, bf16):
     _run(orc, 1, x)
 
 
+@pytest.mark.parametrize("rows,K,bf16", [(32, 8192, True), (64, 4096, False), (65, 4096, False), (33, 2064, False),
+                                          (100, 4992, True)])
+def test_nvfp4_one_launch_grid_path(orc, rows, K, bf16):
+    """Inputs above 256 KB and at most 1 MB take the one-launch path whose
+    workgroups exchange the maximum through the workspace: (32, 8192) BF16 is
+    a 32-row decode activation (512 KB), (64, 4096) FP32 exactly 1 MB, (65,
+    4096) FP32 one row more (two launches), (100, 4992) BF16 ragged in both
+    directions.  Three calls in a row share one workspace, with the maximum
+    in a different place each time: each call must leave the workspace's
+    words zero for the next, so every s_t equals the oracle's."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, rows, 0, K)
+    assert ws is not None and ws.numel() == 16
+    for i, (r, k, big) in enumerate([(-1, -1, 777.0), (0, 0, 12.5), (rows // 2, K // 3, -3.0e4)]):
+        x = synth.gaussian(31 + rows + i, (rows, K))
+        x[r, k] = big
+        if bf16:
+            x = synth.to_bf16_bits(x)
+        say("nvfp4 grid path rows=%d K=%d bf16=%s call %d" % (rows, K, bf16, i))
+        q = fp4.quantize(to_dev(x), fp4.NVFP4, ws=ws)
+        codes, scales, _, ts = orc.quantize(x, 1)
+        assert to_host(q.tensor_scale)[0] == np.float32(ts)
+        np.testing.assert_array_equal(to_host(q.scales), scales)
+        np.testing.assert_array_equal(to_host(q.codes), codes)
+        assert (to_host(ws) == 0).all(), "workspace words left non-zero"
+
+
 def test_nvfp4_tensor_scale_on_large_tensor(orc):
     # many workgroups contribute to the amax; the maximum sits in the last row
     x = synth.gaussian(21, (4096, 1024), every=4099)
@@ -203,12 +231,13 @@ def test_nvfp4_division_sweep_every_scale_byte(orc, s_t):
     assert set(range(1, 127)) <= set(np.unique(canon).tolist())
 
 
-@pytest.mark.parametrize("rows,K", [(16, 4096), (512, 4096)])
+@pytest.mark.parametrize("rows,K", [(16, 4096), (40, 4096), (512, 4096)])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_nvfp4_nan_skipped_by_tensor_maximum(orc, rows, K, bf16):
     """One NaN in the tensor: every path's tensor maximum skips it, as the
-    oracle's does, below the one-launch threshold (256 KB: 16 x 4096) and
-    above it (512 x 4096: amax kernel, then quantise).  s_t and every scale
+    oracle's does, below the one-launch threshold (256 KB: 16 x 4096), on
+    the one-launch grid path (40 x 4096: 320 KB FP32; BF16 160 KB takes the
+    small path) and above 1 MB (512 x 4096: amax kernel, then quantise).  s_t and every scale
     byte equal the oracle's; codes equal everywhere except at the NaN
     itself (a NaN input has no defined code)."""
     x = synth.gaussian(77 + rows, (rows, K))
