@@ -255,13 +255,21 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   } else {
     total = tilesM * tilesN;
   }
+  // Dense persistent: when the tiles leave a last round that fills at most
+  // half the grid, its tiles run as two 128-row halves each (items), so that
+  // every workgroup ends after the same whole tiles plus at most one half
+  // (whose 128 idle rows' waves only copy); e.g. 896 tiles on 256 workgroups:
+  // 768 + 2 x 128 items, 3.5 tiles of work each instead of 4 or 3.
+  const uint32_t tail = !GROUPED && PERSIST && total > gridDim.x ? total % gridDim.x : 0u;
+  const uint32_t first_half = tail != 0u && 2u * tail <= gridDim.x ? total - tail : total;
+  const uint32_t items = total + (total - first_half);
   auto tile_of = [&](uint32_t v, uint32_t& t) -> bool {
     if (GROUPED) {
       t = (v & 7u) * per_xcd + (v >> 3);
       return (v >> 3) < per_xcd && t < total;
     }
     t = v;
-    return v < total;
+    return v < items;
   };
 
   // ---- direct-to-LDS load plan.  One code load (1 KB) fills 8 rows: lane L
@@ -290,11 +298,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       Bx += (size_t)expert * gp.b_codes_stride;
       sBx += (size_t)expert * gp.b_scales_stride;
     } else {
-      uint32_t tm, tn;
-      tile_coords(t, tilesM, tilesN, GROUP_M, tm, tn);
-      m0 = tm * BM;
+      uint32_t tm, tn, tile = t, half = 0u, hrows = BM;
+      if (t >= first_half) {   // item t: half (t - first_half) % 2 of tile first_half + (t - first_half) / 2
+        tile = first_half + ((t - first_half) >> 1);
+        half = (t - first_half) & 1u;
+        hrows = BM / 2u;
+      }
+      tile_coords(tile, tilesM, tilesN, GROUP_M, tm, tn);
+      m0 = tm * BM + half * (BM / 2u);
       n0 = tn * BN;
-      rowsA = (M - m0) < BM ? (M - m0) : BM;
+      rowsA = M > m0 ? ((M - m0) < hrows ? (M - m0) : hrows) : 0u;
     }
     T.m0 = m0;
     T.n0 = n0;
@@ -455,7 +468,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-    for (uint32_t k = 0; k < KT; ++k) {
+    // A half tile's second 128 rows: those waves only take their part of the
+    // stage copies (same waits, barriers and copies as the others).
+    const bool idle = !GROUPED && PERSIST && cur.rowsA <= BM / 2u && wm == 1u;
+    for (uint32_t k = 0; idle && k < KT; ++k) {
+      const uint32_t buf = (g + k) & 1u;
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const bool own = k + 2u < KT;
+      dma(own ? cur : nxt, own ? k + 2u : k + 2u - KT, buf, own || has_next);
+    }
+    for (uint32_t k = 0; !idle && k < KT; ++k) {
       const uint32_t buf = (g + k) & 1u, nbuf = buf ^ 1u;
       read_ops(buf, 1, o1);
       mma_sub<0>(acc, o0, sa, sb);

@@ -570,3 +570,24 @@ def test_bf16_output_is_rne_of_fp32_output(orc, path):
         c16 = to_host(fp4.gemm_grouped(qa, ri, go, codes, scales, N, K, 0, out_dtype=torch.bfloat16))
     assert np.isfinite(c32).all() and np.abs(c32).max() > 0
     np.testing.assert_array_equal(c16.view(np.uint16), _rne_bf16_of(c32))
+
+
+def test_nvfp4_persistent_tail_runs_as_half_tiles(orc):
+    """4096 x 4352 x 256 NVFP4 is 16 x 17 = 272 tiles: on 256 resident
+    workgroups the last 16 tiles (the last tile group: rows 3072-4095,
+    columns 3328-4351) run as 128-row halves, each by a workgroup whose other
+    four waves only copy.  Every element of those 1024 rows, and rows picked
+    from every other 256-row band, against the oracle."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    M, N, K = 4096, 4352, 256
+    a = synth.gaussian(601, (M, K))
+    w = synth.gaussian(602, (N, K), std=0.05)
+    say("nvfp4 persistent tail halves M=%d N=%d K=%d" % (M, N, K))
+    qa, ra_full = _quant_both(orc, a, 1)
+    qw, rw = _quant_both(orc, w, 1)
+    C = to_host(fp4.gemm(qa, qw, out_dtype=torch.bfloat16))
+    rows = np.concatenate([_band_picks(3072, 256, 6), np.arange(3072, 4096)])
+    rr = orc.quantize(a[rows], 1, tensor_scale=ra_full[3])   # the picked rows, under the whole operand's s_t
+    Cref, T = orc.gemm(rr[0], rr[1], rw[0], rw[1], rows.size, N, K, 1, tsA=ra_full[3], tsB=rw[3])
+    assert_gemm_close(orc, C[rows], Cref, T, True, "nvfp4 tail half tiles")
