@@ -6,6 +6,7 @@
 #include "../../include/fp4.h"
 #include "fp4_launch.h"
 
+#include <cstdlib>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,6 +71,17 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
   }
 }
 
+// The one-launch NVFP4 quantiser's wait for the other workgroups is bounded;
+// FP4_TEST_NV_GRID_SPIN (a positive count of sleeps) cuts it short so that
+// tests can run the path a workgroup takes when it stops waiting.  Unset:
+// the kernel's default.
+static uint32_t nv_grid_spin_limit() {
+  const char* e = std::getenv("FP4_TEST_NV_GRID_SPIN");
+  if (!e || !*e) return 0u;
+  const unsigned long v = std::strtoul(e, nullptr, 10);
+  return v == 0ul || v > 0xFFFFFFFFul ? 0u : (uint32_t)v;
+}
+
 static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                          int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,
                          size_t workspace_bytes, uint64_t seed, void* stream) {
@@ -98,7 +110,8 @@ static int quantize_impl(const void* x, int fmt, uint8_t* codes, uint8_t* block_
         fp4::launch_quantize_nv_small(x, in_dtype, codes, block_scales, tensor_scale, rows, K, sr, seed, s));
   if (compute_ts && !twod && fp4::quantize_nv_grid_applies(rows, K, in_dtype))
     return launched(fp4::launch_quantize_nv_grid(x, in_dtype, codes, block_scales, tensor_scale,
-                                                 static_cast<uint32_t*>(workspace), rows, K, sr, seed, 0u, s));
+                                                 static_cast<uint32_t*>(workspace), rows, K, sr, seed,
+                                                 nv_grid_spin_limit(), s));
   if (compute_ts) {
     int rc = launched(fp4::launch_tensor_amax(x, in_dtype, rows * K, static_cast<uint32_t*>(workspace), tensor_scale, s));
     if (rc != FP4_OK) return rc;

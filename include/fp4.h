@@ -154,7 +154,9 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
  *   workspace and wait for each other (a bounded wait, after which a
  *   workgroup reduces the whole maximum itself); larger ones reduce across
  *   workgroups through the workspace, then quantise.  All give the same
- *   bits.)
+ *   bits.  A test hook: the environment variable FP4_TEST_NV_GRID_SPIN, a
+ *   positive count, caps that wait, so that tests reach the path of a
+ *   workgroup that stops waiting.)
  * rows == 0 or K == 0 is a no-op. */
 int fp4_quantize(const void* x, int fmt, uint8_t* codes, uint8_t* block_scales, float* tensor_scale,
                  int64_t rows, int64_t K, int in_dtype, unsigned flags, void* workspace,

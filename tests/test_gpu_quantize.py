@@ -117,6 +117,29 @@ def test_nvfp4_one_launch_grid_path(orc, rows, K, bf16):
         assert (to_host(ws) == 0).all(), "workspace words left non-zero"
 
 
+@pytest.mark.parametrize("rows,K,bf16", [(32, 8192, True), (64, 4096, False)])
+def test_nvfp4_grid_path_wait_cut_short(orc, monkeypatch, rows, K, bf16):
+    """The one-launch path's wait for the other workgroups, cut to one sleep
+    from the host (FP4_TEST_NV_GRID_SPIN): workgroups that stop waiting reduce
+    the whole maximum themselves, the others read the exchanged one.  Either
+    way every bit equals the oracle's, and the workspace ends zero."""
+    import block_scaled_fp4_03_amd as fp4
+    monkeypatch.setenv("FP4_TEST_NV_GRID_SPIN", "1")
+    ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, rows, 0, K)
+    for i in range(2):
+        x = synth.gaussian(41 + rows + i, (rows, K))
+        x[rows - 1 - i, K // (2 + i)] = 99.0 + i
+        if bf16:
+            x = synth.to_bf16_bits(x)
+        say("nvfp4 grid path, wait cut short, rows=%d K=%d bf16=%s call %d" % (rows, K, bf16, i))
+        q = fp4.quantize(to_dev(x), fp4.NVFP4, ws=ws)
+        codes, scales, _, ts = orc.quantize(x, 1)
+        assert to_host(q.tensor_scale)[0] == np.float32(ts)
+        np.testing.assert_array_equal(to_host(q.scales), scales)
+        np.testing.assert_array_equal(to_host(q.codes), codes)
+        assert (to_host(ws) == 0).all(), "workspace words left non-zero"
+
+
 def test_nvfp4_tensor_scale_on_large_tensor(orc):
     # many workgroups contribute to the amax; the maximum sits in the last row
     x = synth.gaussian(21, (4096, 1024), every=4099)
