@@ -68,12 +68,18 @@ struct Ops {
   v4i a[4], b[2];
 };
 
-// MXFP4: 8 MFMAs of one sub-step; op_sel SUB picks the sub-step's scale byte.
-template <int SUB>
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// MXFP4: 8 MFMAs of one sub-step (2 R when only the wave's first R 32-row
+// blocks hold rows); op_sel SUB picks the sub-step's scale byte.
+template <int SUB, int R = 4>
 __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const uint32_t (&sa)[4],
                                         const uint32_t (&sb)[2]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < R; ++r) {
     const v8i a8 = __builtin_shufflevector(o.a[r], o.a[r], 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -87,9 +93,10 @@ __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u
 // NVFP4: the lane's 32 codes of each block split into four groups of 8 (group
 // g lies in the chunk's 16-block g/2), decoded to FP16, one 32x32x16 MFMA per
 // block pair and group.
-template <int SUB>
+template <int SUB, int R = 4>
 __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u32x2 (&sa)[4],
                                         const u32x2 (&sb)[2]) {
+  static_assert(R == 4, "NVFP4 tiles multiply every row block");
   // Scale bytes 2 SUB, 2 SUB + 1 of the lane's 8 (groups 0-1, 2-3) as FP16,
   // two per conversion.
   v2h spa[4], spb[2];
@@ -157,35 +164,57 @@ __device__ __forceinline__ void group_rows(const Groups& gp, int32_t e, uint32_t
   if (hi < lo) hi = lo;
 }
 
-// Locate tile t in the grouped list: tiles of expert e are ceil(cnt_e / BM)
-// m-tiles x tilesN n-tiles, ordered expert by expert.  Returns false past the
-// last tile.  Uniform per workgroup (scalar loads of group_off).  The search
-// starts at the cursor (ecur, fcur) = (expert, its first tile) of the last
-// call, since a workgroup's tiles only increase; t below the cursor restarts
-// it from expert 0.
+// The M-tile of each group.  A group of cnt rows is cut into cnt / 256
+// m-tiles of 256 rows and a last m-tile of the remaining cnt % 256 rows.
+// Inside the kernel a wave multiplies only the 32-row blocks of its 128 rows
+// that hold group rows, so that last m-tile is in effect a 32-, 64-, 128-,
+// 160-, 192- or 256-row tile (16 or fewer rows: 32).  A last m-tile of at
+// most 128 rows keeps half the waves off the matrix core ("light"); every
+// other m-tile is "heavy".
+__device__ __forceinline__ void expert_mtiles(uint32_t cnt, uint32_t& heavy, uint32_t& light) {
+  const uint32_t rem = cnt % BM;
+  light = (rem != 0u && rem <= BM / 2u) ? 1u : 0u;
+  heavy = cnt / BM + (rem > BM / 2u ? 1u : 0u);
+}
+
+// Locate tile t in the grouped list.  The list is cost-first: segment s < E
+// holds expert s's heavy m-tiles x tilesN n-tiles (grouped raster within the
+// expert), segment E + e the n-tiles of expert e's light m-tile, if any.
+// Returns false past the last tile.  Uniform per workgroup (scalar loads of
+// group_off).  The search starts at the cursor (scur, fcur) = (segment, its
+// first tile) of the last call, since a workgroup's tiles only increase; t
+// below the cursor restarts it from segment 0.
 __device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t total_rows, uint32_t t, uint32_t tilesN,
                                              uint32_t& e_out, uint32_t& row0, uint32_t& rows, uint32_t& tm,
-                                             uint32_t& tn, int32_t& ecur, uint32_t& fcur) {
+                                             uint32_t& tn, int32_t& scur, uint32_t& fcur) {
   if (t < fcur) {
-    ecur = 0;
+    scur = 0;
     fcur = 0;
   }
   uint32_t first = fcur;
-  for (int32_t e = ecur; e < gp.E; ++e) {
-    uint32_t lo, hi;
+  for (int32_t s = scur; s < 2 * gp.E; ++s) {
+    const bool heavy_seg = s < gp.E;
+    const int32_t e = heavy_seg ? s : s - gp.E;
+    uint32_t lo, hi, hm, lm;
     group_rows(gp, e, total_rows, lo, hi);
     const uint32_t cnt = hi - lo;
-    const uint32_t mt = (cnt + BM - 1) / BM;
+    expert_mtiles(cnt, hm, lm);
+    const uint32_t mt = heavy_seg ? hm : lm;
     const uint32_t n = mt * tilesN;
     if (t < first + n) {
       uint32_t a, b;
-      raster_coords(t - first, mt, tilesN, GROUP_M, a, b);  // grouped raster within the expert
+      if (heavy_seg) {
+        raster_coords(t - first, mt, tilesN, GROUP_M, a, b);
+      } else {
+        a = hm;             // the light m-tile follows the heavy ones
+        b = t - first;
+      }
       e_out = (uint32_t)e;
       row0 = lo;
       rows = cnt;
       tm = a;
       tn = b;
-      ecur = e;
+      scur = s;
       fcur = first;
       return true;
     }
@@ -194,14 +223,18 @@ __device__ __forceinline__ bool grouped_tile(const Groups& gp, uint32_t total_ro
   return false;
 }
 
-__device__ __forceinline__ uint32_t grouped_total_tiles(const Groups& gp, uint32_t total_rows, uint32_t tilesN) {
-  uint32_t total = 0;
+// Heavy and light tile counts of the grouped list.
+__device__ __forceinline__ void grouped_tile_counts(const Groups& gp, uint32_t total_rows, uint32_t tilesN,
+                                                    uint32_t& heavy, uint32_t& light) {
+  heavy = 0;
+  light = 0;
   for (int32_t e = 0; e < gp.E; ++e) {
-    uint32_t lo, hi;
+    uint32_t lo, hi, hm, lm;
     group_rows(gp, e, total_rows, lo, hi);
-    total += ((hi - lo + BM - 1) / BM) * tilesN;
+    expert_mtiles(hi - lo, hm, lm);
+    heavy += hm * tilesN;
+    light += lm * tilesN;
   }
-  return total;
 }
 
 // Operand addressing of one output tile: scalar bases and byte ranges, plus
@@ -246,12 +279,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 
   // ---- tile schedule.  Workgroup b takes the virtual tiles v = b, b + G, ...
   // (G = grid size, a multiple of 8, so that v % 8 and with it the XCD stay
-  // fixed).  Dense: v -> tile as tile_coords.  Grouped: tiles of the expert
-  // list, v -> t = (v % 8) * ceil(total / 8) + v / 8.
-  uint32_t total, per_xcd = 0;
+  // fixed).  Dense: v -> tile as tile_coords.  Grouped: XCD x = v % 8 owns
+  // the x-th eighth of the heavy tiles followed by the x-th eighth of the
+  // light ones, walked in that order (j = v / 8), so every XCD ends on cheap
+  // tiles, and the first of them go to the workgroups that drew one heavy
+  // tile fewer.
+  uint32_t total, nheavy = 0, nlight = 0;
   if (GROUPED) {
-    total = grouped_total_tiles(gp, M, tilesN);
-    per_xcd = (total + 7u) / 8u;
+    grouped_tile_counts(gp, M, tilesN, nheavy, nlight);
+    total = nheavy + nlight;
   } else {
     total = tilesM * tilesN;
   }
@@ -264,9 +300,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   const uint32_t first_half = tail != 0u && 2u * tail <= gridDim.x ? total - tail : total;
   const uint32_t items = total + (total - first_half);
   auto tile_of = [&](uint32_t v, uint32_t& t) -> bool {
-    if (GROUPED) {
-      t = (v & 7u) * per_xcd + (v >> 3);
-      return (v >> 3) < per_xcd && t < total;
+    if constexpr (GROUPED) {
+      const uint32_t x = v & 7u, j = v >> 3;
+      const uint32_t hx = (nheavy + 7u) >> 3, lx = (nlight + 7u) >> 3;
+      const uint32_t hb = x * hx, lb = x * lx;
+      const uint32_t hc = nheavy > hb ? (nheavy - hb < hx ? nheavy - hb : hx) : 0u;
+      const uint32_t lc = nlight > lb ? (nlight - lb < lx ? nlight - lb : lx) : 0u;
+      if (j < hc) {
+        t = hb + j;
+        return true;
+      }
+      t = nheavy + lb + (j - hc);
+      return j - hc < lc;
     }
     t = v;
     return v < items;
@@ -468,18 +513,68 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
-    // A half tile's second 128 rows: those waves only take their part of the
-    // stage copies (same waits, barriers and copies as the others).
-    const bool idle = !GROUPED && PERSIST && cur.rowsA <= BM / 2u && wm == 1u;
+    // The second 128 rows of a tile of at most 128 rows (a dense half tile, a
+    // grouped light tile): those waves only take their part of the stage
+    // copies (same waits, barriers and copies as the others).  Grouped: a
+    // wave whose 128 rows hold at most 32 (64) group rows multiplies only its
+    // first one (two) 32-row blocks, in a loop of its own with the same waits,
+    // barriers and copies.
+    const bool idle = PERSIST && cur.rowsA <= BM / 2u && wm == 1u;
+    uint32_t nblk = 4u;   // 32-row blocks this wave multiplies
+    if constexpr (GROUPED) {
+      const uint32_t wrows = cur.rowsA > 128u * wm ? cur.rowsA - 128u * wm : 0u;
+      nblk = idle ? 4u : (wrows <= 32u ? 1u : (wrows <= 64u ? 2u : 4u));
+    }
     for (uint32_t k = 0; idle && k < KT; ++k) {
       const uint32_t buf = (g + k) & 1u;
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      if (GROUPED && k == 0u && has_next) gather_offsets(nxt);
       const bool own = k + 2u < KT;
       dma(own ? cur : nxt, own ? k + 2u : k + 2u - KT, buf, own || has_next);
     }
-    for (uint32_t k = 0; !idle && k < KT; ++k) {
+    if constexpr (GROUPED) {
+      // read_ops for a wave that multiplies only its first R 32-row blocks.
+      auto read_ops_n = [&](uint32_t buf, int q, Ops& o, auto rc) {
+        constexpr int R = decltype(rc)::value;
+        const uint8_t* st = lds + buf * STAGE_BYTES;
+#pragma unroll
+        for (int r = 0; r < R; ++r) o.a[r] = *reinterpret_cast<const v4i*>(st + a_rows + 4096u * r + rd[q]);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) o.b[c] = *reinterpret_cast<const v4i*>(st + REGION + b_rows + 4096u * c + rd[q]);
+      };
+      auto short_loop = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        for (uint32_t k = 0; k < KT; ++k) {
+          const uint32_t buf = (g + k) & 1u, nbuf = buf ^ 1u;
+          read_ops_n(buf, 1, o1, rc);
+          mma_sub<0, R>(acc, o0, sa, sb);
+          read_ops_n(buf, 2, o0, rc);
+          mma_sub<1, R>(acc, o1, sa, sb);
+          read_ops_n(buf, 3, o1, rc);
+          mma_sub<2, R>(acc, o0, sa, sb);
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (k == 0u && has_next) gather_offsets(nxt);
+          const bool own = k + 2u < KT;
+          dma(own ? cur : nxt, own ? k + 2u : k + 2u - KT, buf, own || has_next);
+          read_ops_n(nbuf, 0, o0, rc);
+          read_scales(nbuf, sa_n, sb_n);
+          mma_sub<3, R>(acc, o1, sa, sb);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sa[r] = sa_n[r];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) sb[c] = sb_n[c];
+        }
+      };
+      if (nblk == 1u)
+        short_loop(IntC<1>{});
+      else if (nblk == 2u)
+        short_loop(IntC<2>{});
+    }
+    for (uint32_t k = 0; !idle && nblk == 4u && k < KT; ++k) {
       const uint32_t buf = (g + k) & 1u, nbuf = buf ^ 1u;
       read_ops(buf, 1, o1);
       mma_sub<0>(acc, o0, sa, sb);
@@ -760,6 +855,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          // Grouped: 32-row blocks past the group's rows store nothing (a
+          // uniform test instead of 32 masked stores).
+          if (GROUPED && 128u * wm + 32u * (uint32_t)r >= cur.rowsA) continue;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const uint32_t rr = 32u * r + 8u * (i >> 2) + (i & 3);

@@ -395,8 +395,16 @@ def _quant_experts(orc, ws, fmt):
     return codes, scales, refs
 
 
+# Group sizes that reach every per-group M-tile: last m-tiles of 1-32, 33-64,
+# 65-128 rows (light: half the waves idle), 129-160, 161-192, 193-255 rows and
+# whole 256-row tiles, with K of one, two and 11.25 stages.
+_EVERY_MTILE = [140, 170, 200, 250, 64, 65, 32, 33, 128, 129, 0, 256, 385, 16]
+
+
 @pytest.mark.parametrize("counts,N,K", [([5, 0, 33, 2], 96, 128), ([300, 1, 0, 257, 17], 160, 544),
-                                        ([0, 0, 0], 64, 64), ([600], 300, 2880), ([1, 1, 1, 1, 1, 1, 1, 1], 520, 256)])
+                                        ([0, 0, 0], 64, 64), ([600], 300, 2880), ([1, 1, 1, 1, 1, 1, 1, 1], 520, 256),
+                                        (_EVERY_MTILE, 520, 2880), (_EVERY_MTILE, 264, 512),
+                                        (_EVERY_MTILE, 96, 256)])
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_grouped_gemm(orc, counts, N, K, bf16_out):
     import block_scaled_fp4_03_amd as fp4
