@@ -294,8 +294,10 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
  *   each N x K quantised, codes N*K/2 bytes apart and scales
  *   fp4_scale_bytes(fmt, N, K) bytes apart.  C: total_rows x N, row r =
  *   (A[row_idx[r]] . B_e^T) * tsA * tsB for its expert e.
- *   Group sizes stay on the device; the kernel builds its own tile list.
- *   Every row_idx entry must lie in [0, A_rows).
+ *   Group sizes stay on the device; the kernel builds its own tile list: a
+ *   group's last tile is only as high as its rows need (32 to 256 rows, the
+ *   rest of the workgroup idles), and tiles of at most 128 rows run after
+ *   the others.  Every row_idx entry must lie in [0, A_rows).
  * Formats: FP4_MXFP4 and FP4_MXFP4_OCP; FP4_NVFP4 returns FP4_ERR_FMT.
  * Requirements as fp4_gemm, and A's codes (A_rows * K/2 bytes) below 4 GiB;
  *   workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
