@@ -31,7 +31,7 @@ FUNCTIONS = ("fp4_scale_bytes", "fp4_workspace_size", "fp4_quantize", "fp4_quant
              "fp4_quantize_ex",
              "fp4_hadamard16", "fp4_dequantize", "fp4_gemm", "fp4_gemm_ex",
              "fp4_gemm_grouped", "fp4_gemm_nvfp4_act", "fp4_gemm_nvfp4_act_supported", "fp4_gemm_w4a8",
-             "fp4_status_string")
+             "fp4_status_string", "fp4_set_debug")
 
 
 class Fp4Error(RuntimeError):
@@ -49,6 +49,15 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libfp4.so is not built (run python -m block_scaled_fp4_03_amd.build)")
+        # torch first: its HIP runtime then satisfies the library's
+        # libamdhip64.so.7, so both share one runtime (streams, allocations).
+        # Loaded the other way round, torch loads a second copy of the
+        # runtime under another name, and the library's own HIP calls do not
+        # see torch's device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         sig = {
@@ -67,6 +76,7 @@ def lib():
             "fp4_gemm_nvfp4_act_supported": (I32, [I64, I64, I64, I32]),
             "fp4_gemm_w4a8": (I32, [P, P, P, P, P, I32, P, I64, I64, I64, I32, P]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
+            "fp4_set_debug": (I32, [I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -77,6 +87,11 @@ def lib():
 
 
 # ---- raw C-ABI calls (integers for pointers) --------------------------------
+def fp4_set_debug(on):
+    """Debug mode on (1) or off (0); returns the previous setting."""
+    return lib().fp4_set_debug(1 if on else 0)
+
+
 def fp4_status_string(status):
     return lib().fp4_status_string(int(status)).decode()
 

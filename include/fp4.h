@@ -30,7 +30,8 @@
  *   - Argument errors return a negative fp4_status before any HIP call is made,
  *     so they are reported synchronously and leave the stream untouched.  A
  *     failed kernel launch returns FP4_ERR_HIP.  Faults inside a kernel surface
- *     at the caller's next synchronisation.
+ *     at the caller's next synchronisation.  Debug mode (fp4_set_debug,
+ *     FP4_DEBUG) adds checks that make HIP calls and synchronise.
  *   - Matrices are row-major.  A quantised matrix of `rows` x `K` values is
  *       codes:  rows * K/2 bytes; element k of a row is in byte k/2, bits 0-3
  *               for even k and bits 4-7 for odd k; a code is sign<<3 | magnitude
@@ -112,8 +113,26 @@ enum fp4_status {
     FP4_ERR_DTYPE = -5,     /* unknown dtype                                       */
     FP4_ERR_WORKSPACE = -6, /* workspace missing or smaller than required          */
     FP4_ERR_HIP = -7,       /* a HIP launch failed                                 */
-    FP4_ERR_FLAGS = -8      /* unknown flag bits                                   */
+    FP4_ERR_FLAGS = -8,     /* unknown flag bits                                   */
+    FP4_ERR_BOUNDS = -9     /* debug mode only: a buffer is not memory of the      */
+                            /* current device or smaller than the call needs, or   */
+                            /* a group offset or token index is out of range       */
 };
+
+/* Debug mode, for callers hunting a fault or a wrong result: on when the
+ * environment variable FP4_DEBUG is set to anything but "0" when the library
+ * is first used, or after fp4_set_debug(1).  Then every entry point, after its argument checks:
+ *   - checks that each buffer it reads or writes lies wholly inside one device
+ *     allocation of the current device (hipMemGetAddressRange; a caching
+ *     allocator's block counts as one allocation), else FP4_ERR_BOUNDS;
+ *   - fp4_gemm_grouped waits for the stream, copies group_off and row_idx to
+ *     the host and checks them as documented there, else FP4_ERR_BOUNDS;
+ *   - waits for its kernels (hipStreamSynchronize), so that a launch or
+ *     execution error is returned by the call that caused it (FP4_ERR_HIP).
+ * The checks make HIP calls and synchronise, and the grouped check allocates
+ * host memory; none of this happens with debug mode off.  Returns the previous
+ * setting (0 or 1).  Host-only; the setting is process-wide. */
+int fp4_set_debug(int on);
 
 /* Size in bytes of the tiled scale buffer of a rows x K matrix, or a negative
  * fp4_status for an invalid fmt or shape.  Host-only, no HIP call. */

@@ -35,9 +35,24 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(0, -9, -1):
+    for s in range(0, -10, -1):
         assert fp4.fp4_status_string(s).startswith("FP4_")
     assert "unknown" in fp4.fp4_status_string(5)
+    assert "unknown" in fp4.fp4_status_string(-10)
+
+
+def test_debug_mode_switch(L):
+    """fp4_set_debug is host-only and returns the previous setting; argument
+    errors are still reported before any check that would call HIP."""
+    prev = fp4.fp4_set_debug(1)
+    try:
+        assert fp4.fp4_set_debug(1) == 1
+        assert fp4.fp4_quantize(FAKE, 7, FAKE, FAKE, None, 4, 64, 0, 0, None, 0, None) == -4
+        assert fp4.fp4_gemm(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 4, 48, 0, 1, None, 0, None) == -2
+        assert fp4.fp4_set_debug(0) == 1
+        assert fp4.fp4_set_debug(0) == 0
+    finally:
+        fp4.fp4_set_debug(prev)
 
 
 def test_scale_bytes(L):
