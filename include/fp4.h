@@ -32,6 +32,11 @@
  *     failed kernel launch returns FP4_ERR_HIP.  Faults inside a kernel surface
  *     at the caller's next synchronisation.  Debug mode (fp4_set_debug,
  *     FP4_DEBUG) adds checks that make HIP calls and synchronise.
+ *   - Format, dtype, output, activation and operation arguments are declared
+ *     int and take the values of the enums below.  A C enum's underlying type
+ *     is up to the compiler (-fshort-enums makes it one byte), while int is the
+ *     same for every compiler and for foreign-function callers; any other value
+ *     is refused with FP4_ERR_FMT, FP4_ERR_DTYPE or FP4_ERR_FLAGS.
  *   - Matrices are row-major.  A quantised matrix of `rows` x `K` values is
  *       codes:  rows * K/2 bytes; element k of a row is in byte k/2, bits 0-3
  *               for even k and bits 4-7 for odd k; a code is sign<<3 | magnitude
