@@ -437,8 +437,9 @@ def test_grouped_moe_full_size(orc):
     """The MoE workload: 32 experts (5760 x 2880 MXFP4 weights N(0, 0.02^2)),
     16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4.  Every
     row of each expert with at most 256 rows, a whole 256-row band of each
-    larger expert (at a random offset), against one column in each 256-column
-    band, checked against the oracle."""
+    larger expert (at a random offset) and the rows of its last, partial
+    tile, against one column in each 256-column band, checked against the
+    oracle."""
     import block_scaled_fp4_03_amd as fp4
     import torch
     E, N, K, T_rows = 32, 5760, 2880, 16384
@@ -468,7 +469,8 @@ def test_grouped_moe_full_size(orc):
             rs = np.arange(lo, hi)
         else:
             start = lo + int(g.integers(0, hi - lo - 256 + 1))
-            rs = np.arange(start, start + 256)
+            tail = np.arange(lo + (hi - lo) // 256 * 256, hi)     # the last, partial tile
+            rs = np.union1d(np.arange(start, start + 256), tail)
         w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
         rw = orc.quantize(w[cols], 0)
         rx = orc.quantize(x[row_idx[rs]], 0)
