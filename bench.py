@@ -26,6 +26,8 @@ other measured workloads:
   mxfp4_moe               32 experts 5760x2880 MXFP4, 16384 BF16 tokens
                           quantised once per step, Zipf(1.2) top-4 routing;
                           step = quantise + grouped GEMM; TFLOP/s.
+  nvfp4_moe               the same with NVFP4 operands (per-expert tensor
+                          scales); step = amax + quantise + grouped GEMM.
   mxfp4_256               A, B 256x256 FP32; step = quantise A, B + GEMM (FP32
                           out); microseconds.
   mxfp4_quantize_8192     8192x8192 FP32 -> MXFP4; GB/s.
@@ -631,6 +633,41 @@ def mxfp4_moe(torch, fp4, synth):
             "step": "MXFP4 quantise of the 16384 tokens (BF16) + grouped GEMM, BF16 out"}
 
 
+def nvfp4_moe(torch, fp4, synth):
+    """The MoE workload with NVFP4 operands: each expert quantised on its own
+    (its own tensor scale), the tokens quantised per step (tensor amax + NVFP4
+    quantise), the grouped GEMM on the FP16 matrix core."""
+    E, N, K, T = 32, 5760, 2880, 16384
+    counts = synth.zipf_counts()
+    row_idx, off = synth.moe_routing(counts)
+    x = to_dev(torch, synth.mxfp4_moe_act())
+    sbytes = fp4.fp4_scale_bytes(fp4.NVFP4, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        w = synth.mxfp4_moe_weights(E, N, K, experts=[e])[0]
+        fp4.quantize(to_dev(torch, w), fp4.NVFP4,
+                     out=fp4.Quantized(codes[e], scales[e], ts[e:e + 1], fp4.NVFP4, N, K))
+    qx = fp4.quantize(x, fp4.NVFP4)
+    ws = fp4.workspace(fp4.OP_QUANTIZE, fp4.NVFP4, T, 0, K)
+    ri = torch.from_numpy(row_idx).cuda()
+    go = torch.from_numpy(off).cuda()
+    total = int(off[-1])
+    C = torch.empty((total, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp4.quantize(x, fp4.NVFP4, out=qx, ws=ws)
+        fp4.gemm_grouped(qx, ri, go, codes, scales, N, K, fp4.NVFP4, b_tensor_scale=ts, out=C)
+
+    ms = time_steps(torch, step, 10, 2)
+    tf = gemm_flops(total, N, K) / (ms * 1e-3) / 1e12
+    return {"experts": E, "N": N, "K": K, "tokens": T, "routed_rows": total, "ms_per_step": round(ms, 4),
+            "TFLOP_per_s": round(tf, 1), "frac_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4),
+            "step": "tensor amax + NVFP4 quantise of the 16384 tokens (BF16) + grouped NVFP4 GEMM "
+                    "(FP16 matrix core, per-expert tensor scales), BF16 out"}
+
+
 def mxfp4_256(torch, fp4, synth):
     a, b = synth.mxfp4_256()
     xa, xb = to_dev(torch, a), to_dev(torch, b)
@@ -742,6 +779,7 @@ def main():
             ("nvfp4_decode_m32", lambda: nvfp4_decode(torch, fp4, synth, 32)),
             ("nvfp4_mlp", lambda: nvfp4_mlp(torch, fp4, synth)),
             ("mxfp4_moe", lambda: mxfp4_moe(torch, fp4, synth)),
+            ("nvfp4_moe", lambda: nvfp4_moe(torch, fp4, synth)),
             ("mxfp4_256", lambda: mxfp4_256(torch, fp4, synth))]
     for name, fn in todo:
         if args.only is not None and args.only != name:

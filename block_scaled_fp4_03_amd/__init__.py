@@ -429,7 +429,8 @@ def gemm_w4a8(a, b, bias=None, act=ACT_NONE, out_dtype=None, out=None, stream=No
 
 def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_scale=None, out_dtype=None,
                  out=None, ws=None, stream=None):
-    """Grouped (mixture-of-experts) GEMM; see fp4_gemm_grouped in include/fp4.h."""
+    """Grouped (mixture-of-experts) GEMM; see fp4_gemm_grouped in include/fp4.h.
+    NVFP4: b_tensor_scale holds one float32 per expert."""
     torch = _torch()
     dev = _need_q(a, "a").codes.device
     if a.K != K or a.fmt != fmt:
@@ -445,8 +446,10 @@ def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_s
         raise Fp4Error(int(nscale), "fp4_scale_bytes")
     _need(b_codes, "b_codes", (torch.uint8,), E * N * (K // 2), dev)
     _need(b_scales, "b_scales", (torch.uint8,), E * nscale, dev)
+    if fmt == NVFP4 and (a.tensor_scale is None or b_tensor_scale is None):
+        raise ValueError("NVFP4 needs a's tensor scale and b_tensor_scale (one float32 per expert)")
     if b_tensor_scale is not None:
-        _need(b_tensor_scale, "b_tensor_scale", (torch.float32,), 1, dev)
+        _need(b_tensor_scale, "b_tensor_scale", (torch.float32,), E if fmt == NVFP4 else 1, dev)
     if out is None:
         out = torch.empty((total, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=dev)
     _need_out(out, "out", (total, N), (torch.float32, torch.bfloat16), dev)

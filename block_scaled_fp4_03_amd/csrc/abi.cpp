@@ -457,6 +457,8 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
   if (debug_on()) {
     int rc = debug_buffers({{A, code_bytes(fmt, A_rows, K)},
                             {sA, (uint64_t)fp4_scale_bytes(fmt, A_rows, K)},
+                            {fmt == FP4_NVFP4 ? tsA : nullptr, 4u},
+                            {fmt == FP4_NVFP4 ? tsB : nullptr, (uint64_t)E * 4u},
                             {row_idx, (uint64_t)total_rows * 4u},
                             {group_off, ((uint64_t)E + 1u) * 4u},
                             {B, (uint64_t)E * code_bytes(fmt, N, K)},

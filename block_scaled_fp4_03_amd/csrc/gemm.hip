@@ -248,6 +248,7 @@ struct TileAddr {
   uint32_t m0, n0, rowsA, row0;
   uint32_t voffA[4];
   uint32_t svoffA;
+  uint32_t expert;   // grouped: the tile's expert
 };
 
 // PERSIST: workgroups walk tiles (grid <= resident workgroups) with the next
@@ -322,6 +323,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   // (L%8) ^ ((row >> 1) & 7).  Wave w loads row groups w + 8q (q < 4) of A and
   // of B and scale tile w of A and of B.
   const uint32_t grow = lane >> 3;
+  // Grouped: the tile row whose scale bytes this lane copies (see gather_offsets).
+  const uint32_t scale_row = FMT == kFmtNV ? lane >> 1 : lane & 31u;
   const uint32_t gchunk = (lane & 7u) ^ ((4u * (wave & 1u) + (lane >> 4)) & 7u);
   uint32_t voffB[4];
   const uint32_t svoffB = (wave * KT) * STILE + lane * 4u;
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
     T.n0 = n0;
     T.rowsA = rowsA;
     T.row0 = row0;
+    if constexpr (GROUPED) T.expert = expert;
     const uint32_t rowsB = (N - n0) < BN ? (N - n0) : BN;
     T.b_tile = Bx + (size_t)n0 * ldb;
     T.b_bytes = rowsB * ldb;
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
         const uint32_t r = 8u * (wave + 8u * q) + grow;
         T.voffA[q] = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
       }
-      const uint32_t r = 32u * wave + (lane & 31u);
+      const uint32_t r = 32u * wave + scale_row;
       T.svoffA = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
       T.sa_base = sA;
       T.sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
@@ -391,9 +395,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
   };
 
   // Grouped: the loaded token indices of T become its lane offsets; rows
-  // past the group get an out-of-range offset and load zeros.  Scale dwords:
-  // lane L = 32j + i of scale block `wave` is row i, chunk parity j, found at
-  // the gathered row's own scale tile.
+  // past the group get an out-of-range offset and load zeros.  Scale dwords
+  // of scale block `wave`, each taken from the gathered row's own scale tile:
+  // MXFP4: lane L = 32j + i copies entry (row i, chunk parity j), 4 bytes;
+  // NVFP4: lane L copies dword L % 2 of entry (row L / 2, parity h) of 8
+  // bytes, h the half of the 512-byte tile being copied (its copy adds 256 h).
   auto gather_offsets = [&](TileAddr& T) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -401,8 +407,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       T.voffA[q] = r < T.rowsA ? T.voffA[q] * ldb + 16u * gchunk : 0x80000000u;
     }
     const uint32_t tok = T.svoffA;
-    T.svoffA = 32u * wave + (lane & 31u) < T.rowsA ? (tok >> 5) * srow + ((lane & 32u) + (tok & 31u)) * 4u
-                                                   : 0x80000000u;
+    const uint32_t in_tile = FMT == kFmtNV ? (tok & 31u) * 8u + (lane & 1u) * 4u : ((lane & 32u) + (tok & 31u)) * 4u;
+    T.svoffA = 32u * wave + scale_row < T.rowsA ? (tok >> 5) * srow + in_tile : 0x80000000u;
   };
 
   // Copy stage `stage_k` of tile T into LDS buffer `buf`; stages past K (or
@@ -428,7 +434,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (uint32_t h = 0; h < STILE / 256u; ++h) {
       // NVFP4 lanes own 8 bytes: the two halves of a 512-byte tile are lanes
-      // 0-31 and 32-63 of the dword copy.  (Grouped NVFP4 is not offered.)
+      // 0-31 and 32-63 of the dword copy.
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + 2u * REGION + STILE * wave + 256u * h), 4,
                                                (GROUPED ? T.svoffA : svoffB) + 256u * h, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + 2u * REGION + SCALE_REGION + STILE * wave + 256u * h),
@@ -520,8 +526,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
     // first one (two) 32-row blocks, in a loop of its own with the same waits,
     // barriers and copies.
     const bool idle = PERSIST && cur.rowsA <= BM / 2u && wm == 1u;
-    uint32_t nblk = 4u;   // 32-row blocks this wave multiplies
-    if constexpr (GROUPED) {
+    uint32_t nblk = 4u;   // 32-row blocks this wave multiplies (MXFP4)
+    if constexpr (GROUPED && FMT == kFmtMX) {
       const uint32_t wrows = cur.rowsA > 128u * wm ? cur.rowsA - 128u * wm : 0u;
       nblk = idle ? 4u : (wrows <= 32u ? 1u : (wrows <= 64u ? 2u : 4u));
     }
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       const bool own = k + 2u < KT;
       dma(own ? cur : nxt, own ? k + 2u : k + 2u - KT, buf, own || has_next);
     }
-    if constexpr (GROUPED) {
+    if constexpr (GROUPED && FMT == kFmtMX) {
       // read_ops for a wave that multiplies only its first R 32-row blocks.
       auto read_ops_n = [&](uint32_t buf, int q, Ops& o, auto rc) {
         constexpr int R = decltype(rc)::value;
@@ -640,8 +646,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
         bcol[c] = col < N ? bias[col] : 0.0f;
       }
     }
+    // Grouped NVFP4: each expert's weights carry their own tensor scale.
+    float tile_scale = scale;
+    if constexpr (GROUPED && FMT == kFmtNV) tile_scale = sload(tsA) * sload(tsB + cur.expert);
     auto epi = [&](float a, int c) {
-      float v = a * scale;
+      float v = a * tile_scale;
       if (use_bias) v = v + bcol[c];
       if (use_act) v = v > 0.0f ? v : 0.0f;
       return v;
@@ -977,7 +986,7 @@ hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const
 
 size_t gemm_grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
 
-bool gemm_grouped_supports(int fmt) { return fmt != kFmtNV; }
+bool gemm_grouped_supports(int) { return true; }
 
 hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                                const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
@@ -992,7 +1001,10 @@ hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_ro
   const uint32_t KT = (uint32_t)((K + 255) / 256);
   const size_t scale_stride = (size_t)((N + 31) / 32) * KT * (fmt == kFmtNV ? 512u : 256u);
   const Groups gp{row_idx, group_off, E, (uint32_t)A_rows, (size_t)N * (size_t)(K / 2), scale_stride};
-  (void)fmt;
+  if (fmt == kFmtNV)   // tsB: one tensor scale per expert
+    return launch<kFmtNV, true, true, false>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C,
+                                             (uint32_t)total_rows, (uint32_t)N, (uint32_t)K, 0, tilesN, gp, nullptr,
+                                             0u, nullptr, nullptr, stream);
   return launch<kFmtMX, true, true, false>(dim3((uint32_t)grid), out_dtype, A, sA, B, sB, tsA, tsB, C, (uint32_t)total_rows,
                                     (uint32_t)N, (uint32_t)K, 0, tilesN, gp, nullptr, 0u, nullptr, nullptr,
                                     stream);

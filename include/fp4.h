@@ -322,7 +322,10 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
  *   group's last tile is only as high as its rows need (32 to 256 rows, the
  *   rest of the workgroup idles), and tiles of at most 128 rows run after
  *   the others.  Every row_idx entry must lie in [0, A_rows).
- * Formats: FP4_MXFP4 and FP4_MXFP4_OCP; FP4_NVFP4 returns FP4_ERR_FMT.
+ * Formats: FP4_MXFP4, FP4_MXFP4_OCP and FP4_NVFP4.  NVFP4: tsA is the token
+ *   matrix's tensor scale (one device FP32) and tsB holds E device FP32
+ *   values, expert e's tensor scale at tsB[e] (each expert quantised on its
+ *   own); both required (FP4_ERR_NULL).  MXFP4: both ignored, may be NULL.
  * Requirements as fp4_gemm, and A's codes (A_rows * K/2 bytes) below 4 GiB;
  *   workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
  *   fmt, total_rows, N, K, E) bytes (0 today). */

@@ -151,6 +151,8 @@ def test_grouped_argument_errors(L):
                  a["C"], a["total"], a["N"], a["K"], a["fmt"], a["out"], None, 0, None)
 
     assert call(fmt=3) == -4
+    assert call(fmt=1) == -1                    # NVFP4 without tensor scales
+    assert call(fmt=1, tsA=FAKE, tsB=FAKE + 2) == -3
     assert call(K=40) == -2
     assert call(E=-1) == -2
     assert call(total=0) == 0

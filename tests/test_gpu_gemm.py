@@ -433,6 +433,54 @@ def test_grouped_gemm(orc, counts, N, K, bf16_out):
     assert_gemm_close(orc, Cg.reshape(-1), Cref, T, bf16_out, "grouped")
 
 
+@pytest.mark.parametrize("counts,N,K", [([5, 0, 33, 2], 96, 128), ([300, 1, 0, 257, 17], 160, 544),
+                                        (_EVERY_MTILE, 264, 512), ([600], 300, 2880)])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_grouped_gemm_nvfp4(orc, counts, N, K, bf16_out):
+    """NVFP4 experts, each quantised on its own (its own tensor scale, tsB[e]),
+    against NVFP4 tokens: every output element against the oracle, expert by
+    expert with that expert's tensor scale.  Weights of each expert have a
+    different spread, so the tensor scales differ."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    fmt = fp4.NVFP4
+    counts = np.array(counts)
+    E = counts.size
+    T_rows = max(64, int(counts.max()))
+    row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=int(counts.sum()) + N + 1)
+    x = synth.to_bf16_bits(synth.gaussian(70 + N, (T_rows, K)))
+    say("grouped nvfp4 counts=%s N=%d K=%d" % (counts.tolist(), N, K))
+    qa, ra = _quant_both(orc, x, fmt)
+    assert to_host(qa.tensor_scale)[0] == np.float32(ra[3])
+    sbytes = fp4.fp4_scale_bytes(fmt, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(E, dtype=torch.float32, device="cuda")
+    ref_ts = []
+    for e in range(E):
+        w = synth.gaussian(95 + e, (N, K), std=0.02 * (1 + e), bernoulli=0.001)
+        fp4.quantize(to_dev(w), fmt, out=fp4.Quantized(codes[e], scales[e], ts[e:e + 1], fmt, N, K))
+        r = orc.quantize(w, fmt)
+        np.testing.assert_array_equal(to_host(codes[e]), r[0])
+        np.testing.assert_array_equal(to_host(scales[e]), r[1])
+        assert to_host(ts[e:e + 1])[0] == np.float32(r[3])
+        ref_ts.append(r[3])
+    C = fp4.gemm_grouped(qa, torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda(), codes, scales, N, K,
+                         fmt, b_tensor_scale=ts, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+    Cg = to_host(C)
+    B = to_host(codes).reshape(-1)
+    sB = to_host(scales).reshape(-1)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.repeat(np.arange(lo, hi), N)
+        cols = np.tile(np.arange(N), hi - lo)
+        Cref, T = orc.gemm_grouped_sampled(ra[0], ra[1], T_rows, row_idx, off, B, sB, N, K, fmt, rows, cols,
+                                           tsA=ra[3], tsB=ref_ts[e])
+        assert_gemm_close(orc, Cg[lo:hi].reshape(-1), Cref, T, bf16_out, "grouped nvfp4 expert %d" % e)
+
+
 def test_grouped_moe_full_size(orc):
     """The MoE workload: 32 experts (5760 x 2880 MXFP4 weights N(0, 0.02^2)),
     16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4.  Every

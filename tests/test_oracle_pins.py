@@ -297,30 +297,37 @@ def test_gemm_equals_numpy_matmul_of_dequantised(orc, fmt, M, N, K):
     np.testing.assert_array_equal(Ts, T[rows, cols])
 
 
-def test_grouped_equals_per_expert_gemm(orc):
-    fmt, E, T_rows, N, K = 0, 4, 24, 16, 96
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_grouped_equals_per_expert_gemm(orc, fmt):
+    """The grouped oracle equals the dense oracle on each expert's gathered
+    rows.  NVFP4: the gathered rows are quantised under the whole token
+    matrix's tensor scale (so their codes and block scales are those of the
+    whole matrix), and each expert's rows use that expert's tensor scale."""
+    E, T_rows, N, K = 4, 24, 16, 96
     counts = np.array([5, 0, 17, 2])
     row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=1)
     x = synth.gaussian(40, (T_rows, K))
-    A, sA, _, _ = orc.quantize(x, fmt)
-    Bs, sBs = [], []
+    A, sA, _, tsA = orc.quantize(x, fmt)
+    Bs, sBs, tsBs = [], [], []
     for e in range(E):
-        b, s, _, _ = orc.quantize(synth.gaussian(50 + e, (N, K), std=0.02), fmt)
+        b, s, _, t = orc.quantize(synth.gaussian(50 + e, (N, K), std=0.02 * (1 + e)), fmt)
         Bs.append(b)
         sBs.append(s)
+        tsBs.append(t)
     B = np.concatenate([b.reshape(-1) for b in Bs])
     sB = np.concatenate(sBs)
-    rows = np.repeat(np.arange(off[-1]), N)
-    cols = np.tile(np.arange(N), off[-1])
-    C, T = orc.gemm_grouped_sampled(A, sA, T_rows, row_idx, off, B, sB, N, K, fmt, rows, cols)
-    C = C.reshape(off[-1], N)
     for e in range(E):
         if counts[e] == 0:
             continue
-        g = row_idx[off[e]:off[e + 1]]
-        Ag = orc.quantize(x[g], fmt)
-        Ce, _ = orc.gemm(Ag[0], Ag[1], Bs[e], sBs[e], len(g), N, K, fmt)
-        np.testing.assert_array_equal(C[off[e]:off[e + 1]], Ce)
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.repeat(np.arange(lo, hi), N)
+        cols = np.tile(np.arange(N), hi - lo)
+        C, _ = orc.gemm_grouped_sampled(A, sA, T_rows, row_idx, off, B, sB, N, K, fmt, rows, cols,
+                                        tsA=tsA, tsB=tsBs[e])
+        g = row_idx[lo:hi]
+        Ag = orc.quantize(x[g], fmt, tensor_scale=tsA if fmt == 1 else None)
+        Ce, _ = orc.gemm(Ag[0], Ag[1], Bs[e], sBs[e], len(g), N, K, fmt, tsA=tsA, tsB=tsBs[e])
+        np.testing.assert_array_equal(C.reshape(hi - lo, N), Ce)
 
 
 def test_tolerance_check_semantics(orc):
