@@ -96,12 +96,11 @@ __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u
 template <int SUB, int R = 4>
 __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u32x2 (&sa)[4],
                                         const u32x2 (&sb)[2]) {
-  static_assert(R == 4, "NVFP4 tiles multiply every row block");
   // Scale bytes 2 SUB, 2 SUB + 1 of the lane's 8 (groups 0-1, 2-3) as FP16,
   // two per conversion.
   v2h spa[4], spb[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < R; ++r)
     spa[r] = (SUB & 1) ? e4m3x2_to_f16<true>(sa[r][SUB >> 1]) : e4m3x2_to_f16<false>(sa[r][SUB >> 1]);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -110,11 +109,11 @@ __device__ __forceinline__ void mma_sub(v16f (&acc)[4][2], const Ops& o, const u
   for (int g = 0; g < 4; ++g) {
     v8h a[4], b[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = decode8((uint32_t)o.a[r][g], g < 2 ? splat_lo(spa[r]) : splat_hi(spa[r]));
+    for (int r = 0; r < R; ++r) a[r] = decode8((uint32_t)o.a[r][g], g < 2 ? splat_lo(spa[r]) : splat_hi(spa[r]));
 #pragma unroll
     for (int c = 0; c < 2; ++c) b[c] = decode8((uint32_t)o.b[c][g], g < 2 ? splat_lo(spb[c]) : splat_hi(spb[c]));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[r], b[c], acc[r][c], 0, 0, 0);
   }
@@ -526,8 +525,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
     // first one (two) 32-row blocks, in a loop of its own with the same waits,
     // barriers and copies.
     const bool idle = PERSIST && cur.rowsA <= BM / 2u && wm == 1u;
-    uint32_t nblk = 4u;   // 32-row blocks this wave multiplies (MXFP4)
-    if constexpr (GROUPED && FMT == kFmtMX) {
+    uint32_t nblk = 4u;   // 32-row blocks this wave multiplies
+    if constexpr (GROUPED) {
       const uint32_t wrows = cur.rowsA > 128u * wm ? cur.rowsA - 128u * wm : 0u;
       nblk = idle ? 4u : (wrows <= 32u ? 1u : (wrows <= 64u ? 2u : 4u));
     }
@@ -540,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
       const bool own = k + 2u < KT;
       dma(own ? cur : nxt, own ? k + 2u : k + 2u - KT, buf, own || has_next);
     }
-    if constexpr (GROUPED && FMT == kFmtMX) {
+    if constexpr (GROUPED) {
       // read_ops for a wave that multiplies only its first R 32-row blocks.
       auto read_ops_n = [&](uint32_t buf, int q, Ops& o, auto rc) {
         constexpr int R = decltype(rc)::value;
