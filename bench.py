@@ -19,8 +19,8 @@ other measured workloads:
   nvfp4_decode_m{1,8,32}  W 8192x8192 NVFP4 (pre-quantised), X Mx8192 BF16
                           quantised on the fly; step = tensor amax + quantise
                           + decode GEMV (one fused kernel at M = 1, two
-                          kernels at M = 8, three at M = 32); GB/s of
-                          algorithmic bytes vs 8 TB/s.
+                          kernels at M = 8 and 32); GB/s of algorithmic
+                          bytes vs 8 TB/s.
   nvfp4_mlp               A 4096x4096 BF16 quantised on the fly, W 14336x4096
                           NVFP4; step = amax + quantise + GEMM; TFLOP/s.
   mxfp4_moe               32 experts 5760x2880 MXFP4, 16384 BF16 tokens
