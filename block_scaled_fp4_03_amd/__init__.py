@@ -428,9 +428,11 @@ def gemm_w4a8(a, b, bias=None, act=ACT_NONE, out_dtype=None, out=None, stream=No
 
 
 def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_scale=None, out_dtype=None,
-                 out=None, ws=None, stream=None):
+                 out=None, ws=None, stream=None, pregather=True):
     """Grouped (mixture-of-experts) GEMM; see fp4_gemm_grouped in include/fp4.h.
-    NVFP4: b_tensor_scale holds one float32 per expert."""
+    NVFP4: b_tensor_scale holds one float32 per expert.  pregather: pass a
+    workspace (ws, or one allocated here) so that the call first copies the
+    token rows into expert order; False runs the GEMM on the gathered rows."""
     torch = _torch()
     dev = _need_q(a, "a").codes.device
     if a.K != K or a.fmt != fmt:
@@ -453,8 +455,11 @@ def gemm_grouped(a, row_idx, group_off, b_codes, b_scales, N, K, fmt, b_tensor_s
     if out is None:
         out = torch.empty((total, N), dtype=torch.bfloat16 if out_dtype is None else out_dtype, device=dev)
     _need_out(out, "out", (total, N), (torch.float32, torch.bfloat16), dev)
-    if ws is None:
-        ws = workspace(OP_GEMM_GROUPED, fmt, total, N, K, E, device=dev)
+    if not pregather:
+        ws = None
+    elif ws is None:
+        n = fp4_workspace_size(OP_GEMM_GROUPED, fmt, total, N, K, E)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None   # no control words: not zeroed
     else:
         _need(ws, "ws", (torch.uint8,), None, dev)
     rc = fp4_gemm_grouped(_ptr(a.codes), _ptr(a.scales), a.rows, _ptr(row_idx), _ptr(group_off), E, _ptr(b_codes),

@@ -192,7 +192,9 @@ size_t fp4_workspace_size(int op, int fmt, int64_t M, int64_t N, int64_t K, int3
     case FP4_OP_GEMM:
       return 0;
     case FP4_OP_GEMM_GROUPED:
-      return fp4::gemm_grouped_workspace(M, N, K, E);
+      // Optional: the token rows gathered into expert order.
+      if (!fmt_ok(fmt) || M < 0 || K < 0 || K % 32 != 0) return 0;
+      return fp4::gemm_grouped_workspace(fmt, M, N, K, E);
     default:
       return 0;
   }
@@ -451,9 +453,12 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
       !aligned(group_off, 4) || !aligned(tsA, 4) || !aligned(tsB, 4))
     return FP4_ERR_ALIGN;
   if (!aligned(C, out_dtype == FP4_F32 ? 4 : 2)) return FP4_ERR_ALIGN;
-  const size_t need = fp4::gemm_grouped_workspace(total_rows, N, K, E);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return FP4_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 16)) return FP4_ERR_ALIGN;
+  // The workspace is optional: NULL runs the GEMM on gathered rows; one of at
+  // least fp4_workspace_size bytes first copies the rows into expert order.
+  const size_t need = fp4::gemm_grouped_workspace(fmt, total_rows, N, K, E);
+  if (workspace && workspace_bytes < need) return FP4_ERR_WORKSPACE;
+  if (workspace && !aligned(workspace, 16)) return FP4_ERR_ALIGN;
+  if (workspace && (uint64_t)total_rows * (uint64_t)(K / 2) > (uint64_t)kMaxRange) return FP4_ERR_SHAPE;
   if (debug_on()) {
     int rc = debug_buffers({{A, code_bytes(fmt, A_rows, K)},
                             {sA, (uint64_t)fp4_scale_bytes(fmt, A_rows, K)},
@@ -464,7 +469,7 @@ int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const 
                             {B, (uint64_t)E * code_bytes(fmt, N, K)},
                             {sB, (uint64_t)E * (uint64_t)fp4_scale_bytes(fmt, N, K)},
                             {C, (uint64_t)total_rows * (uint64_t)N * elem_bytes(out_dtype)},
-                            {need > 0 ? workspace : nullptr, need}});
+                            {workspace, need}});
     if (rc == FP4_OK) rc = debug_groups(row_idx, group_off, E, total_rows, A_rows, as_stream(stream));
     if (rc != FP4_OK) return rc;
   }

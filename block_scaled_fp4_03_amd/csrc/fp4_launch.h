@@ -61,7 +61,9 @@ hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const
 
 // Grouped (mixture-of-experts) GEMM over the same tiles (gemm.hip).
 bool gemm_grouped_supports(int fmt);
-size_t gemm_grouped_workspace(int64_t total_rows, int64_t N, int64_t K, int32_t E);
+// Bytes of the optional workspace: the token rows gathered into output-row
+// order (codes, then scale tiles).
+size_t gemm_grouped_workspace(int fmt, int64_t total_rows, int64_t N, int64_t K, int32_t E);
 hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                                const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
                                const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N,

@@ -135,7 +135,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 
 // Grouped problem description (device pointers).
 struct Groups {
-  const int32_t* row_idx;    // output row -> A row
+  const int32_t* row_idx;    // output row -> A row (NULL: A is in output-row order)
   const int32_t* group_off;  // E + 1 prefix offsets of the output rows
   int32_t E;
   uint32_t A_rows;           // rows of A (tokens)
@@ -377,10 +377,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t r = 8u * (wave + 8u * q) + grow;
-        T.voffA[q] = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
+        const uint32_t o = row0 + m0 + (r < rowsA ? r : 0u);
+        T.voffA[q] = gp.row_idx ? (uint32_t)gp.row_idx[o] : o;
       }
       const uint32_t r = 32u * wave + scale_row;
-      T.svoffA = (uint32_t)gp.row_idx[row0 + m0 + (r < rowsA ? r : 0u)];
+      const uint32_t o = row0 + m0 + (r < rowsA ? r : 0u);
+      T.svoffA = gp.row_idx ? (uint32_t)gp.row_idx[o] : o;
       T.sa_base = sA;
       T.sa_bytes = ((gp.A_rows + 31u) / 32u) * srow;
     } else {
@@ -983,15 +985,94 @@ hipError_t launch_gemm_tiled(int fmt, const uint8_t* A, const uint8_t* sA, const
   return launch_gemm_ex(fmt, A, sA, B, sB, tsA, tsB, nullptr, 0, C, nullptr, nullptr, M, N, K, out_dtype, stream);
 }
 
-size_t gemm_grouped_workspace(int64_t, int64_t, int64_t, int32_t) { return 0; }
+namespace {
+
+// Token rows gathered into output-row order (the grouped GEMM's optional
+// pre-pass): row r of (Ag, sAg) = row row_idx[r] of (A, sA), codes and scale
+// entries (ENT bytes: 4 for MXFP4; 8 would serve NVFP4), in the same tiled
+// layout.
+// One wave per row of the 32-row-padded output; padding rows get zero scale
+// entries and no codes.  Reads go through buffer ranges (an index outside A
+// reads zeros).
+template <uint32_t ENT>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+                                                          uint32_t A_rows, const int32_t* __restrict__ row_idx,
+                                                          uint32_t total, uint32_t K, uint8_t* __restrict__ Ag,
+                                                          uint8_t* __restrict__ sAg) {
+  constexpr uint32_t STILE = 64u * ENT;            // 32 rows x 2 entries of ENT bytes
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t r = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t total_pad = (total + 31u) & ~31u;
+  if (r >= total_pad) return;
+  const bool live = r < total;
+  const uint32_t ldb = K / 2u, KT = (K + 255u) / 256u;
+  const int32_t si = live ? row_idx[r] : 0;
+  const uint32_t src = (uint32_t)si;
+  const bool ok = live && si >= 0 && src < A_rows;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, A_rows * ldb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sA, ((A_rows + 31u) / 32u) * KT * STILE);
+  if (live) {
+    for (uint32_t off = 16u * lane; off < ldb; off += 1024u) {
+      const v4i c = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? src * ldb + off : 0x80000000u, 0, 0));
+      *reinterpret_cast<v4i*>(Ag + (size_t)r * ldb + off) = c;
+    }
+  }
+  for (uint32_t e = lane; e < 2u * KT; e += 64u) {
+    const uint32_t kt = e >> 1, j = e & 1u;
+    const uint32_t so = ((src >> 5) * KT + kt) * STILE + (32u * j + (src & 31u)) * ENT;
+    uint8_t* dst = sAg + ((size_t)(r >> 5) * KT + kt) * STILE + (32u * j + (r & 31u)) * ENT;
+    if (ENT == 4u) {
+      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? so : 0x80000000u, 0, 0);
+    } else {
+      *reinterpret_cast<u32x2*>(dst) =
+          __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? so : 0x80000000u, 0, 0));
+    }
+  }
+}
+
+// Bytes of the gathered codes (padded to 256) and of their scale tiles.
+size_t gathered_code_bytes(int64_t total_rows, int64_t K) {
+  return ((size_t)total_rows * (size_t)(K / 2) + 255u) & ~(size_t)255u;
+}
+size_t gathered_scale_bytes(int fmt, int64_t total_rows, int64_t K) {
+  return (size_t)((total_rows + 31) / 32) * (size_t)((K + 255) / 256) * (fmt == kFmtNV ? 512u : 256u);
+}
+
+}  // namespace
+
+// MXFP4 only: the NVFP4 GEMM's stages are long enough (FP16 matrix core) to
+// hide the gathered rows' latency, and there the copy cost more than it saved
+// (MoE step 1.97-1.99 -> 1.99-2.01 ms, against 0.82-0.83 -> 0.78-0.79 ms for
+// MXFP4).
+size_t gemm_grouped_workspace(int fmt, int64_t total_rows, int64_t, int64_t K, int32_t) {
+  if (fmt == kFmtNV) return 0;
+  return gathered_code_bytes(total_rows, K) + gathered_scale_bytes(fmt, total_rows, K);
+}
 
 bool gemm_grouped_supports(int) { return true; }
 
 hipError_t launch_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                                const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
                                const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N,
-                               int64_t K, int fmt, int out_dtype, void* /*workspace*/, hipStream_t stream) {
+                               int64_t K, int fmt, int out_dtype, void* workspace, hipStream_t stream) {
   const uint32_t tilesN = (uint32_t)((N + BN - 1) / BN);
+  // With a workspace: gather the token rows into output-row order first, so
+  // that the GEMM reads contiguous rows (a tile's scale entries then come
+  // from whole 32-row tiles instead of one scale tile per gathered row).
+  if (workspace != nullptr && total_rows > 0 && fmt != kFmtNV) {
+    uint8_t* Ag = static_cast<uint8_t*>(workspace);
+    uint8_t* sAg = Ag + gathered_code_bytes(total_rows, K);
+    const uint32_t total_pad = (uint32_t)((total_rows + 31) / 32 * 32);
+    const dim3 ggrid((total_pad + 3u) / 4u);
+    gather_rows_kernel<4u><<<ggrid, dim3(256), 0, stream>>>(A, sA, (uint32_t)A_rows, row_idx, (uint32_t)total_rows,
+                                                             (uint32_t)K, Ag, sAg);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    A = Ag;
+    sA = sAg;
+    A_rows = total_rows;
+    row_idx = nullptr;
+  }
   // Upper bound on the tile count (each expert rounds up at most once), a
   // multiple of 8 so the XCD-contiguous order covers every tile; workgroups
   // past the real count return at once.

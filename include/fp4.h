@@ -145,9 +145,12 @@ int64_t fp4_scale_bytes(int fmt, int64_t rows, int64_t K);
 
 /* Workspace bytes an operation needs (0 if none).  For FP4_OP_QUANTIZE, M is
  * the row count; for FP4_OP_GEMM_GROUPED, E is the expert count and M the total
- * routed rows.  Today only NVFP4 quantisation that computes its own tensor
- * scale needs one (16 bytes: the running amax and two workgroup counters);
- * GEMMs return 0.  Operations keep their control words at the start of the
+ * routed rows.  NVFP4 quantisation that computes its own tensor scale needs 16
+ * bytes (the running amax and two workgroup counters); fp4_gemm returns 0.
+ * FP4_OP_GEMM_GROUPED returns the size of an OPTIONAL workspace (MXFP4
+ * formats; 0 for NVFP4): given one, fp4_gemm_grouped first copies the routed
+ * token rows into expert order there, which makes the GEMM faster; it needs
+ * no zero-fill (it holds no control words).  Operations keep their control words at the start of the
  * workspace.  A workspace must be zero-filled once before its first use; every
  * call leaves the control words zero again when its work on the stream
  * completes, so one zero-filled workspace of the largest size needed serves
@@ -326,9 +329,14 @@ int fp4_gemm(const uint8_t* A, const uint8_t* sA, const uint8_t* B, const uint8_
  *   matrix's tensor scale (one device FP32) and tsB holds E device FP32
  *   values, expert e's tensor scale at tsB[e] (each expert quantised on its
  *   own); both required (FP4_ERR_NULL).  MXFP4: both ignored, may be NULL.
- * Requirements as fp4_gemm, and A's codes (A_rows * K/2 bytes) below 4 GiB;
- *   workspace fp4_workspace_size(FP4_OP_GEMM_GROUPED,
- *   fmt, total_rows, N, K, E) bytes (0 today). */
+ * Requirements as fp4_gemm, and A's codes (A_rows * K/2 bytes) below 4 GiB.
+ * workspace (optional, MXFP4 formats): NULL, or at least
+ *   fp4_workspace_size(FP4_OP_GEMM_GROUPED, fmt, total_rows, N, K, E) bytes,
+ *   16-byte aligned (else FP4_ERR_WORKSPACE / FP4_ERR_ALIGN), with the
+ *   gathered codes (total_rows * K/2 bytes) below 4 GiB.  With it, the call
+ *   first copies row_idx's token rows (codes and scales) into expert order
+ *   there and the GEMM reads them as contiguous rows; the result has the same
+ *   bits.  Ignored for NVFP4.  Calls sharing one workspace must be ordered. */
 int fp4_gemm_grouped(const uint8_t* A, const uint8_t* sA, int64_t A_rows, const int32_t* row_idx,
                      const int32_t* group_off, int32_t E, const uint8_t* B, const uint8_t* sB,
                      const float* tsA, const float* tsB, void* C, int64_t total_rows, int64_t N, int64_t K,

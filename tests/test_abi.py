@@ -78,6 +78,14 @@ def test_workspace_sizes(L):
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.MXFP4, 8192, 8192, 8192) == 0
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 1, 8192, 8192) == 0
     assert fp4.fp4_workspace_size(fp4.OP_GEMM, fp4.NVFP4, 32, 8192, 8192) == 0
+    # Grouped (optional): the routed token rows in expert order, codes padded
+    # to 256 bytes, then their scale tiles.
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, fp4.MXFP4, 65536, 5760, 2880, 32) == \
+        65536 * 1440 + 2048 * 12 * 256
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, fp4.MXFP4_OCP, 100, 64, 544, 3) == \
+        (100 * 272 + 255) // 256 * 256 + 4 * 3 * 256
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, fp4.NVFP4, 100, 64, 544, 3) == 0   # gathers in the GEMM
+    assert fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, fp4.MXFP4, 8, 16, 40, 2) == 0   # K % 32
 
 
 FAKE = 0x100000  # 16-byte-aligned fake device address: never dereferenced on the error paths
@@ -145,10 +153,10 @@ def test_grouped_argument_errors(L):
 
     def call(**kw):
         a = dict(A=FAKE, sA=FAKE, A_rows=8, row_idx=FAKE, off=FAKE, E=2, B=FAKE, sB=FAKE, tsA=None, tsB=None, C=FAKE,
-                 total=8, N=16, K=64, fmt=0, out=1)
+                 total=8, N=16, K=64, fmt=0, out=1, ws=None, wsb=0)
         a.update(kw)
         return g(a["A"], a["sA"], a["A_rows"], a["row_idx"], a["off"], a["E"], a["B"], a["sB"], a["tsA"], a["tsB"],
-                 a["C"], a["total"], a["N"], a["K"], a["fmt"], a["out"], None, 0, None)
+                 a["C"], a["total"], a["N"], a["K"], a["fmt"], a["out"], a["ws"], a["wsb"], None)
 
     assert call(fmt=3) == -4
     assert call(fmt=1) == -1                    # NVFP4 without tensor scales
@@ -158,6 +166,11 @@ def test_grouped_argument_errors(L):
     assert call(total=0) == 0
     assert call(row_idx=None) == -1
     assert call(off=FAKE + 2) == -3
+    # The optional workspace: too small, misaligned.
+    need = fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, 0, 8, 16, 64, 2)
+    assert need > 0
+    assert call(ws=FAKE, wsb=need - 1) == -6
+    assert call(ws=FAKE + 8, wsb=need) == -3
 
 
 def test_fused_decode_argument_errors(L):

@@ -406,7 +406,8 @@ _EVERY_MTILE = [140, 170, 200, 250, 64, 65, 32, 33, 128, 129, 0, 256, 385, 16]
                                         (_EVERY_MTILE, 520, 2880), (_EVERY_MTILE, 264, 512),
                                         (_EVERY_MTILE, 96, 256)])
 @pytest.mark.parametrize("bf16_out", [False, True])
-def test_grouped_gemm(orc, counts, N, K, bf16_out):
+@pytest.mark.parametrize("pregather", [True, False])
+def test_grouped_gemm(orc, counts, N, K, bf16_out, pregather):
     import block_scaled_fp4_03_amd as fp4
     import torch
     fmt = 0
@@ -415,12 +416,12 @@ def test_grouped_gemm(orc, counts, N, K, bf16_out):
     row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=int(counts.sum()) + N)
     x = synth.to_bf16_bits(synth.gaussian(80 + N, (T_rows, K)))
     ws = [synth.gaussian(90 + e, (N, K), std=0.02) for e in range(counts.size)]
-    say("grouped counts=%s N=%d K=%d" % (counts.tolist(), N, K))
+    say("grouped counts=%s N=%d K=%d pregather=%s" % (counts.tolist(), N, K, pregather))
     qa, ra = _quant_both(orc, x, fmt)
     codes, scales, _ = _quant_experts(orc, ws, fmt)
     total = int(off[-1])
     C = fp4.gemm_grouped(qa, torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda(), codes, scales, N, K,
-                         fmt, out_dtype=torch.bfloat16 if bf16_out else torch.float32)
+                         fmt, out_dtype=torch.bfloat16 if bf16_out else torch.float32, pregather=pregather)
     if total == 0:
         assert C.numel() == 0
         return
@@ -481,6 +482,37 @@ def test_grouped_gemm_nvfp4(orc, counts, N, K, bf16_out):
         assert_gemm_close(orc, Cg[lo:hi].reshape(-1), Cref, T, bf16_out, "grouped nvfp4 expert %d" % e)
 
 
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_grouped_pregather_bit_equal(orc, fmt):
+    """The two MXFP4 grouped paths -- token rows copied into expert order in
+    the workspace first, or gathered by the GEMM itself -- return the same bits
+    (same products in the same order), also with padding rows past the end
+    of the 32-row scale tiles and a token matrix smaller than the routed
+    rows."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    counts = np.array([70, 0, 257, 3, 33, 129])
+    E, N, K = counts.size, 264, 544
+    T_rows = 100
+    row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=11)
+    x = synth.to_bf16_bits(synth.gaussian(12, (T_rows, K)))
+    qa = fp4.quantize(to_dev(x), fmt)
+    sbytes = fp4.fp4_scale_bytes(fmt, N, K)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, sbytes), dtype=torch.uint8, device="cuda")
+    ts = torch.empty(E, dtype=torch.float32, device="cuda") if fmt == 1 else None
+    for e in range(E):
+        w = synth.gaussian(13 + e, (N, K), std=0.02)
+        fp4.quantize(to_dev(w), fmt, out=fp4.Quantized(codes[e], scales[e], ts[e:e + 1] if fmt == 1 else None,
+                                                       fmt, N, K))
+    ri, go = torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda()
+    say("grouped pregather vs gather fmt=%d" % fmt)
+    for dt in (torch.float32, torch.bfloat16):
+        c1 = fp4.gemm_grouped(qa, ri, go, codes, scales, N, K, fmt, b_tensor_scale=ts, out_dtype=dt, pregather=True)
+        c0 = fp4.gemm_grouped(qa, ri, go, codes, scales, N, K, fmt, b_tensor_scale=ts, out_dtype=dt, pregather=False)
+        assert np.array_equal(to_host(c1).view(np.uint8), to_host(c0).view(np.uint8))
+
+
 def test_grouped_moe_full_size(orc):
     """The MoE workload: 32 experts (5760 x 2880 MXFP4 weights N(0, 0.02^2)),
     16384 BF16 tokens quantised once, Zipf(1.2) routing with top-4.  Every
@@ -529,7 +561,8 @@ def test_grouped_moe_full_size(orc):
 
 
 @pytest.mark.parametrize("offsets", [[0, 60, 40, 130], [0, -10, 50, 100], [0, 30, 30, 2 ** 31 - 1]])
-def test_grouped_malformed_offsets_stay_in_bounds(orc, offsets):
+@pytest.mark.parametrize("with_ws", [False, True])
+def test_grouped_malformed_offsets_stay_in_bounds(orc, offsets, with_ws):
     """group_off that decreases, goes negative or runs past total_rows: the
     kernel clamps every group to [0, total_rows], so nothing past C's
     total_rows rows is written.  C and row_idx are allocated with guard rows
@@ -547,10 +580,13 @@ def test_grouped_malformed_offsets_stay_in_bounds(orc, offsets):
     off = np.array(offsets, np.int64).astype(np.int32)
     ri_d, off_d = to_dev(ri), to_dev(off)
     C = torch.full((total + guard, N), 1234.5, dtype=torch.float32, device="cuda")
-    say("grouped malformed offsets %s" % offsets)
+    nws = fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, 0, total, N, K, E) if with_ws else 0
+    wsp = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    say("grouped malformed offsets %s workspace %d" % (offsets, nws))
     rc = fp4.fp4_gemm_grouped(qa.codes.data_ptr(), qa.scales.data_ptr(), T_rows, ri_d.data_ptr(), off_d.data_ptr(),
                               E, codes.data_ptr(), scales.data_ptr(), None, None, C.data_ptr(), total, N, K, 0,
-                              fp4.F32, None, 0, torch.cuda.current_stream().cuda_stream)
+                              fp4.F32, wsp.data_ptr() if with_ws else None, nws,
+                              torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     Ch = to_host(C)
     assert (Ch[total:] == np.float32(1234.5)).all(), "rows past total_rows were written"
