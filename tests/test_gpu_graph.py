@@ -165,3 +165,51 @@ def test_graph_w4a8_step(orc):
     gr = _capture(step, 2)
     other = torch.randn(M, K, device="cuda").to(torch.bfloat16)
     _replay_and_check(gr, C, ref, lambda: fp4.gemm_w4a8(fp4.quantize(other, fp4.MXFP8), qw))
+
+
+def test_graph_grouped_moe_step(orc):
+    """The MoE step at a small size -- BF16 tokens -> MXFP4, then the grouped
+    GEMM with its workspace (two kernels: the copy of the routed rows into
+    expert order, the GEMM) -- captured twice in one graph; every replay
+    equals the eager result, which is checked against the oracle."""
+    import block_scaled_fp4_03_amd as fp4
+    import torch
+    counts = np.array([70, 0, 257, 3, 33])
+    E, N, K, T_rows = counts.size, 264, 544, 120
+    row_idx, off = synth.moe_routing(counts, tokens=T_rows, seed=21)
+    x = synth.to_bf16_bits(synth.gaussian(22, (T_rows, K)))
+    say("graph grouped moe step")
+    xd = to_dev(x)
+    qx = fp4.quantize(xd, fp4.MXFP4)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, fp4.fp4_scale_bytes(0, N, K)), dtype=torch.uint8, device="cuda")
+    wsr = []
+    for e in range(E):
+        w = synth.gaussian(23 + e, (N, K), std=0.02)
+        fp4.quantize(to_dev(w), 0, out=fp4.Quantized(codes[e], scales[e], None, 0, N, K))
+        wsr.append(w)
+    total = int(off[-1])
+    ri, go = torch.from_numpy(row_idx).cuda(), torch.from_numpy(off).cuda()
+    ws = torch.empty(fp4.fp4_workspace_size(fp4.OP_GEMM_GROUPED, 0, total, N, K, E), dtype=torch.uint8,
+                     device="cuda")
+    C = torch.empty((total, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp4.quantize(xd, fp4.MXFP4, out=qx)
+        fp4.gemm_grouped(qx, ri, go, codes, scales, N, K, 0, out=C, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = C.clone()
+    rx = orc.quantize(x, orc.FMT_MXFP4)
+    B = to_host(codes).reshape(-1)
+    sB = to_host(scales).reshape(-1)
+    rows = np.repeat(np.arange(total), N)
+    cols = np.tile(np.arange(N), total)
+    Cref, T = orc.gemm_grouped_sampled(rx[0], rx[1], T_rows, row_idx, off, B, sB, N, K, orc.FMT_MXFP4, rows, cols)
+    assert_gemm_close(orc, to_host(C).reshape(-1), Cref, T, False, "eager grouped")
+
+    g = _capture(step, 2)
+    other = torch.randn(T_rows, K, device="cuda")
+    _replay_and_check(g, C, ref, lambda: fp4.gemm_grouped(fp4.quantize(other, fp4.MXFP4), ri, go, codes, scales, N,
+                                                          K, 0, ws=ws, out_dtype=torch.float32))
